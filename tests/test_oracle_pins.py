@@ -1,0 +1,382 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Every check here compares the oracle with a library routine, brute force, a
+closed form, a hand-worked example under tests/golden/, or an identity that a
+dropped term, a wrong sign, a wrong index or a transposed operand would break.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+from scipy.spatial.distance import cdist
+from scipy.special import softmax
+
+from oracle import loopvq_oracle as O
+from synth import gen, workloads as W
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------
+# Encode: brute force vs scipy vs an exhaustive loop; hand example
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(6))
+def test_encode_matches_cdist_and_exhaustive_loop(seed):
+    r = _rng(seed)
+    K, E, n = int(r.integers(1, 40)), int(r.integers(1, 9)), 50
+    C = np.round(r.normal(size=(K, E)) * 4) / 4          # coarse grid -> real ties
+    if K > 3:
+        C[K - 1] = C[1]                                   # duplicated codeword
+    x = np.round(r.normal(size=(n, E)) * 4) / 4
+    idx, d1, d2 = O.encode(x, C, chunk=7)
+    ref = cdist(x, C, "sqeuclidean")
+    assert np.array_equal(idx, ref.argmin(axis=1))       # argmin: first occurrence
+    for i in range(n):
+        best_k, best_d = 0, None
+        for k in range(K):
+            dk = sum((float(x[i, e]) - float(C[k, e])) ** 2 for e in range(E))
+            if best_d is None or dk < best_d:
+                best_k, best_d = k, dk
+        assert idx[i] == best_k
+        assert d1[i] == pytest.approx(best_d, abs=1e-12)
+        others = sorted(ref[i, k] for k in range(K) if k != best_k)
+        if others:
+            assert d2[i] == pytest.approx(others[0], abs=1e-12)
+
+
+def test_encode_duplicated_codeword_picks_lowest():
+    C = np.array([[1.0, 2.0], [3.0, 4.0], [1.0, 2.0], [3.0, 4.0]])
+    idx, d1, d2 = O.encode(np.array([[1.0, 2.0], [3.0, 4.1]]), C)
+    assert list(idx) == [0, 1]
+    assert d1[0] == 0.0 and d2[0] == 0.0
+    assert O.near_tie(d1, d2).tolist() == [True, True]
+
+
+def test_encode_hand_example():
+    g = json.load(open(os.path.join(GOLD, "hand_encode.json")))
+    C = np.array(g["codebook"], dtype=np.float64)
+    for case in g["cases"]:
+        x = np.array([case["x"]], dtype=np.float64)
+        assert np.array_equal(O.sq_dists(x, C)[0], np.array(case["dist"]))
+        idx, d1, _ = O.encode(x, C)
+        assert idx[0] == case["idx"]
+        assert d1[0] == min(case["dist"])
+
+
+def test_encode_single_codeword():
+    idx, d1, d2 = O.encode(_rng(1).normal(size=(9, 5)), np.zeros((1, 5)))
+    assert (idx == 0).all() and np.isinf(d2).all()
+
+
+# ---------------------------------------------------------------------------
+# Bits per element (closed form) and page sizes
+# ---------------------------------------------------------------------------
+def test_bits_per_elem_closed_form():
+    assert O.bits_per_elem(2, 1, 2) == 1.0                 # K=4, c=1, G=2
+    expect = {"tiny_d64_n512": 0.5, "layer16h_d128_b32_n4k": 0.5, "stack24x4_h16_d128_b64_n32k": 0.5,
+              "stack24x4_c8_rot_b128_n16k": 0.25, "deep4x32_h32_d128_b16_n8k": 0.5}
+    for wl in W.ALL:
+        assert O.bits_per_elem(wl.index_bits, wl.chans, wl.loop_group) == expect[wl.name]
+        assert np.log2(wl.codewords) / (wl.chans * wl.loop_group) == expect[wl.name]
+
+
+@pytest.mark.parametrize("b,PT,NG", [(8, 64, 32), (8, 64, 16), (3, 16, 8), (9, 128, 4)])
+def test_page_bytes_closed_form(b, PT, NG):
+    lay = O.page_layout(PT, NG, b)
+    # index bits of PT tokens x NG groups x 2 kinds, in bytes
+    assert lay["page_bytes"] * 8 == 2 * PT * NG * b
+    n = 3 * PT - 5
+    r = _rng(b)
+    ik = r.integers(0, 1 << b, (n, NG))
+    iv = r.integers(0, 1 << b, (n, NG))
+    pages = O.pack_sequence(ik, iv, PT, b)
+    assert pages.shape == (3, lay["page_bytes"])
+
+
+def test_config_checks():
+    O.check_config(4, 4, 16, 16, 128, 4, 8)
+    for bad in [dict(T=6, G=4), dict(d=130, c=4), dict(Hq=3, Hkv=2), dict(b=17), dict(b=0), dict(d=24, c=4)]:
+        kw = dict(T=4, G=4, Hq=16, Hkv=16, d=128, c=4, b=8)
+        kw.update(bad)
+        with pytest.raises(ValueError):
+            O.check_config(**kw)
+
+
+# ---------------------------------------------------------------------------
+# Packing: hand-worked bytes, independent big-integer formulation, round trips
+# ---------------------------------------------------------------------------
+def test_pack_tile_hand_examples():
+    g = json.load(open(os.path.join(GOLD, "pack_tiles.json")))
+    for case in g["cases"]:
+        b, vals, want = case["b"], case["vals"], bytes.fromhex(case["bytes"])
+        assert O.pack_tile(vals, b) == want
+        assert O.unpack_tile(want, b) == vals
+        assert O.pack_tiles(np.array([vals]), b).tobytes() == want
+        assert O.unpack_tiles(np.frombuffer(want, dtype=np.uint8)[None], b)[0].tolist() == vals
+
+
+@settings(max_examples=200, deadline=None)
+@given(b=st.integers(1, 16), data=st.data())
+def test_pack_roundtrip_and_bigint(b, data):
+    vals = data.draw(st.lists(st.integers(0, (1 << b) - 1), min_size=16, max_size=16))
+    packed = O.pack_tile(vals, b)
+    as_int = sum(v << (e * b) for e, v in enumerate(vals))   # little-endian integer view
+    assert packed == as_int.to_bytes(2 * b, "little")
+    assert O.unpack_tile(packed, b) == vals
+    assert O.unpack_tiles(O.pack_tiles(np.array([vals]), b), b)[0].tolist() == vals
+
+
+def test_pack_rejects_out_of_range():
+    with pytest.raises(ValueError):
+        O.pack_tile([256] + [0] * 15, 8)
+    with pytest.raises(ValueError):
+        O.pack_tiles(np.full((1, 16), -1), 4)
+
+
+@pytest.mark.parametrize("b,PT,NG,n", [(8, 64, 32, 201), (8, 64, 16, 64), (5, 16, 8, 33), (9, 32, 4, 1), (8, 64, 32, 0)])
+def test_sequence_roundtrip_layout_and_padding(b, PT, NG, n):
+    r = _rng(n + b)
+    ik = r.integers(0, 1 << b, (n, NG))
+    iv = r.integers(0, 1 << b, (n, NG))
+    pages = O.pack_sequence(ik, iv, PT, b)
+    k2, v2 = O.unpack_sequence(pages, n, NG, PT, b)
+    assert np.array_equal(k2, ik) and np.array_equal(v2, iv)
+    lay = O.page_layout(PT, NG, b)
+    # location of one index, written out from the layout description
+    for (u, g, kind) in [(0, 0, 0), (n - 1, NG - 1, 1), (n // 2, NG // 3, 0)] if n else []:
+        page, w = divmod(u, PT)
+        Q, i = divmod(w, 4)
+        uq, rr = divmod(g, 4)
+        tile_off = kind * lay["kind_bytes"] + (Q * (NG // 4) + uq) * lay["tile_bytes"]
+        tile = pages[page, tile_off:tile_off + lay["tile_bytes"]].tobytes()
+        e = 4 * i + rr
+        as_int = int.from_bytes(tile, "little")
+        want = (ik if kind == 0 else iv)[u, g]
+        assert (as_int >> (e * b)) & ((1 << b) - 1) == want
+    # padding tokens of the last page are zero bits
+    if n % PT:
+        k_pad, v_pad = O.unpack_sequence(pages, pages.shape[0] * PT, NG, PT, b)
+        assert (k_pad[n:] == 0).all() and (v_pad[n:] == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# Sub-vectors and dequantization
+# ---------------------------------------------------------------------------
+def test_subvector_order_written_out():
+    G, n, d, c = 4, 3, 16, 4
+    planes = np.arange(G * n * d, dtype=np.float64).reshape(G, n, d)
+    x = O.subvectors(planes, c)
+    for tok, g, tau, i in itertools.product(range(n), range(d // c), range(G), range(c)):
+        assert x[tok, g, tau * c + i] == planes[tau, tok, g * c + i]
+
+
+def test_generator_codebook_rows_are_subvectors_of_fresh_tokens():
+    wl = W.TINY
+    cb = gen.codebooks(wl, 0)                      # [L][Jcb][H][NG][K][E]
+    tok = gen.codebook_tokens(wl, 0, 0, 0)         # [K][T][d]
+    planes = gen.bf16_to_f64(tok[:, :wl.loop_group, :]).transpose(1, 0, 2)   # [G][K][d]
+    x = O.subvectors(planes, wl.chans)             # [K][NG][E]
+    assert np.array_equal(gen.bf16_to_f64(cb[0, 0, 0]), x.transpose(1, 0, 2))
+
+
+def test_dequantize_inverts_exact_codebook_encode():
+    r = _rng(3)
+    G, n, d, c = 4, 40, 32, 4
+    planes = r.normal(size=(G, n, d))
+    x = O.subvectors(planes, c)
+    NG = d // c
+    # codebook per group = the data sub-vectors in a shuffled order, plus far fillers
+    C = np.empty((NG, 64, c * G))
+    for g in range(NG):
+        C[g, :n] = x[r.permutation(n), g]
+        C[g, n:] = 100 + r.normal(size=(64 - n, c * G))
+    idx = np.stack([O.encode(x[:, g], C[g])[0] for g in range(NG)], axis=1)
+    for tau in range(G):
+        assert np.array_equal(O.dequantize(idx, C, tau, c), planes[tau])
+
+
+# ---------------------------------------------------------------------------
+# Attention: textbook softmax, exact codebook, special cases, invariants
+# ---------------------------------------------------------------------------
+def _plain_attention(q, keys, vals, scale):
+    p = softmax(scale * (keys @ q))
+    return p @ vals, np.log(np.exp(scale * (keys @ q)).sum())
+
+
+def test_attention_matches_scipy_softmax():
+    r = _rng(5)
+    q, keys, vals = r.normal(size=16), r.normal(size=(37, 16)), r.normal(size=(37, 16))
+    o, lse = O.attention(q, keys, vals, 0.25)
+    o2, lse2 = _plain_attention(q, keys, vals, 0.25)
+    assert np.allclose(o, o2, rtol=1e-13, atol=1e-14)
+    assert lse == pytest.approx(lse2, rel=1e-13)
+
+
+def _exact_codebook_case(b, seed, P=3, R=5, n_vq=20, d=16, c=4, G=4):
+    """Cache whose vector-quantized rows are all codewords: VQ attention == plain bf16 attention."""
+    r = _rng(seed)
+    K = 1 << b
+    NG = d // c
+    tau = int(r.integers(0, G))
+    planes = gen.bf16_to_f64(gen.to_bf16_bits(r.normal(size=(G, n_vq, d))))
+    x = O.subvectors(planes, c)
+    C = np.empty((NG, K, c * G))
+    slot = r.permutation(K)[:n_vq]
+    for g in range(NG):
+        C[g] = gen.bf16_to_f64(gen.to_bf16_bits(r.normal(size=(K, c * G)) * 50 + 200))
+        C[g, slot] = x[:, g]
+    idx_k = np.stack([O.encode(x[:, g], C[g])[0] for g in range(NG)], axis=1)
+    # pack and unpack through the page format on the way
+    pages = O.pack_sequence(idx_k, idx_k, 8, b)
+    idx_k2, _ = O.unpack_sequence(pages, n_vq, NG, 8, b)
+    kp, vp = r.normal(size=(P, d)), r.normal(size=(P, d))
+    kr, vr = r.normal(size=(R, d)), r.normal(size=(R, d))
+    q = r.normal(size=d)
+    vals_tau = planes[tau] * 0.5 - 1.0
+    # values: use a second exact codebook built the same way
+    xv = O.subvectors(planes * 0.5 - 1.0, c)
+    Cv = C.copy()
+    for g in range(NG):
+        Cv[g, slot] = xv[:, g]
+    idx_v = np.stack([O.encode(xv[:, g], Cv[g])[0] for g in range(NG)], axis=1)
+    return dict(q=q, kp=kp, vp=vp, kr=kr, vr=vr, planes=planes, vals_tau=vals_tau, tau=tau,
+                idx_k=idx_k2, idx_v=idx_v, C=C, Cv=Cv, c=c)
+
+
+@pytest.mark.parametrize("b,seed", [(8, 0), (8, 1), (9, 2), (6, 3)])
+def test_exact_codebook_reproduces_plain_attention(b, seed):
+    e = _exact_codebook_case(b, seed)
+    assert np.array_equal(O.dequantize(e["idx_k"], e["C"], e["tau"], e["c"]), e["planes"][e["tau"]])
+    o, lse = O.decode_query(e["q"], e["kp"], e["vp"], e["idx_k"], e["idx_v"], e["C"], e["Cv"],
+                            e["kr"], e["vr"], e["tau"], e["c"], 0.3)
+    keys = np.concatenate([e["kp"], e["planes"][e["tau"]], e["kr"]])
+    vals = np.concatenate([e["vp"], e["vals_tau"], e["vr"]])
+    o2, lse2 = _plain_attention(e["q"], keys, vals, 0.3)
+    assert np.allclose(o, o2, rtol=1e-12, atol=1e-12)
+    assert lse == pytest.approx(lse2, rel=1e-12)
+
+
+def test_context_split():
+    assert O.split_context(512, 8, 64) == (8, 440, 64)
+    assert O.split_context(72, 8, 64) == (8, 0, 64)
+    assert O.split_context(73, 8, 64) == (8, 1, 64)
+    assert O.split_context(5, 8, 64) == (5, 0, 0)
+    assert O.split_context(1, 8, 64) == (1, 0, 0)
+    assert O.split_context(40, 8, 64) == (8, 0, 32)
+
+
+def test_no_vq_tokens_is_plain_attention():
+    r = _rng(7)
+    d = 8
+    kp, vp, kr, vr = r.normal(size=(8, d)), r.normal(size=(8, d)), r.normal(size=(20, d)), r.normal(size=(20, d))
+    q = r.normal(size=d)
+    empty = np.zeros((0, 2), dtype=np.int64)
+    C = r.normal(size=(2, 4, 16))
+    o, _ = O.decode_query(q, kp, vp, empty, empty, C, C, kr, vr, 1, 4, 0.5)
+    o2, _ = _plain_attention(q, np.concatenate([kp, kr]), np.concatenate([vp, vr]), 0.5)
+    assert np.allclose(o, o2, rtol=1e-13, atol=1e-14)
+
+
+def test_zero_query_gives_mean_of_values():
+    r = _rng(8)
+    d, c, G, NG, K = 16, 4, 4, 4, 16
+    C, Cv = r.normal(size=(NG, K, c * G)), r.normal(size=(NG, K, c * G))
+    ik, iv = r.integers(0, K, (30, NG)), r.integers(0, K, (30, NG))
+    kp, vp, kr, vr = (r.normal(size=(8, d)), r.normal(size=(8, d)),
+                      r.normal(size=(11, d)), r.normal(size=(11, d)))
+    o, lse = O.decode_query(np.zeros(d), kp, vp, ik, iv, C, Cv, kr, vr, 2, c, 0.1)
+    vals = np.concatenate([vp, O.dequantize(iv, Cv, 2, c), vr])
+    assert np.allclose(o, vals.mean(axis=0), rtol=1e-13, atol=1e-14)
+    assert lse == pytest.approx(np.log(49), rel=1e-14)
+
+
+def test_single_token_gives_its_value_row():
+    r = _rng(9)
+    d = 8
+    empty = np.zeros((0, 2), dtype=np.int64)
+    C = r.normal(size=(2, 4, 16))
+    kp, vp = r.normal(size=(1, d)), r.normal(size=(1, d))
+    o, lse = O.decode_query(r.normal(size=d), kp, vp, empty, empty, C, C,
+                            np.zeros((0, d)), np.zeros((0, d)), 0, 4, 1.0)
+    assert np.array_equal(o, vp[0])
+
+
+def test_rotation_identity_and_orthogonal_invariance():
+    r = _rng(10)
+    d = 32
+    q, keys, vals = r.normal(size=d), r.normal(size=(25, d)), r.normal(size=(25, d))
+    o0, l0 = O.attention(q, keys, vals, 0.2)
+    o1, l1 = O.attention(q, keys, vals, 0.2, rot=np.eye(d))
+    assert np.array_equal(o0, o1) and l0 == l1
+    Qm, Rm = np.linalg.qr(r.normal(size=(d, d)))
+    Qm = Qm * np.sign(np.diag(Rm))                  # Haar-distributed orthogonal matrix
+    o2, l2 = O.attention(q, keys @ Qm, vals, 0.2, rot=Qm)   # keys stored as Q^T k (row form k Q)
+    assert np.allclose(o2, o0, rtol=1e-12, atol=1e-13)
+    assert l2 == pytest.approx(l0, rel=1e-12)
+    # a wrongly transposed rotation breaks it
+    o3, _ = O.attention(q, keys @ Qm, vals, 0.2, rot=Qm.T)
+    assert not np.allclose(o3, o0, rtol=1e-6)
+
+
+def test_generator_rotation_is_orthogonal_and_matches_dense_form():
+    wl = W.QUARTER_16K.with_(head_dim=16, chans=4, layers=1, kv_heads=1, batch=1, context=10)
+    R = gen.rotation_matrix_f32(wl).astype(np.float64)
+    assert np.allclose(R @ R.T, np.eye(16), atol=1e-6)
+    # keys generated rotated equal R^T applied to the unrotated keys (up to bf16 rounding)
+    k_rot = gen.bf16_to_f64(gen.kv_tokens(wl, 0, 0, 0, 0, 0, 10, 0, 4))
+    k_raw = gen.bf16_to_f64(gen.kv_tokens(wl.with_(rotate_keys=False), 0, 0, 0, 0, 0, 10, 0, 4))
+    want = k_raw @ R                                   # row form of R^T k
+    assert np.allclose(k_rot, want, rtol=2e-2, atol=2e-2 * np.abs(want).max())
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_permutation_and_window_order_invariance(seed):
+    r = _rng(20 + seed)
+    d, c, G, NG, K, n = 16, 4, 4, 4, 32, 50
+    C, Cv = r.normal(size=(NG, K, c * G)), r.normal(size=(NG, K, c * G))
+    ik, iv = r.integers(0, K, (n, NG)), r.integers(0, K, (n, NG))
+    kp, vp, kr, vr = (r.normal(size=(8, d)), r.normal(size=(8, d)),
+                      r.normal(size=(13, d)), r.normal(size=(13, d)))
+    q = r.normal(size=d)
+    o, lse = O.decode_query(q, kp, vp, ik, iv, C, Cv, kr, vr, 3, c, 0.3)
+    p, w = r.permutation(n), r.permutation(13)
+    o2, lse2 = O.decode_query(q, kp, vp, ik[p], iv[p], C, Cv, kr[w], vr[w], 3, c, 0.3)
+    assert np.allclose(o2, o, rtol=1e-14, atol=1e-14)
+    assert lse2 == pytest.approx(lse, rel=1e-14)
+    # permuting key indices without their value indices is a different cache
+    o3, _ = O.decode_query(q, kp, vp, ik[p], iv, C, Cv, kr, vr, 3, c, 0.3)
+    assert not np.allclose(o3, o, rtol=1e-6)
+
+
+def test_lut_score_equals_dequantized_dot_product():
+    """Score of a VQ token as a sum over groups of (q-slice . codeword-slice) lookups."""
+    r = _rng(30)
+    d, c, G, NG, K, n, tau = 32, 4, 4, 8, 64, 40, 2
+    C = r.normal(size=(NG, K, c * G))
+    idx = r.integers(0, K, (n, NG))
+    q = r.normal(size=d)
+    lut = np.array([[q[g * c:(g + 1) * c] @ C[g, k, tau * c:(tau + 1) * c] for g in range(NG)]
+                    for k in range(K)])                 # [K][NG]
+    s_lut = np.array([sum(lut[idx[m, g], g] for g in range(NG)) for m in range(n)])
+    s_deq = O.dequantize(idx, C, tau, c) @ q
+    assert np.allclose(s_lut, s_deq, rtol=1e-12, atol=1e-12)
+
+
+def test_indices_in_range_after_encode():
+    r = _rng(31)
+    C = r.normal(size=(16, 8))
+    idx, _, _ = O.encode(r.normal(size=(100, 8)), C)
+    assert idx.min() >= 0 and idx.max() < 16
+
+
+def test_near_tie_rule():
+    d1 = np.array([1.0, 1.0, 0.0, 2.0])
+    d2 = np.array([1.0 + 5e-7, 1.0 + 2e-6, 0.0, 3.0])
+    assert O.near_tie(d1, d2).tolist() == [True, False, True, False]
