@@ -1,0 +1,215 @@
+/*
+ * loopvq.h - C ABI of the LoopVQ decode-attention / encode library (MI355X, gfx950).
+ *
+ * LoopVQ ("LoopVQ: Sub 1-bit KV Cache Quantization for Looped Transformers",
+ * arXiv 2611.05304; English abstract on the shd-paper.top listing) stores the
+ * per-loop-step KV cache of a looped transformer as codebook indices: one
+ * b-bit index covers c channels of G consecutive loop steps (airadar.tv
+ * summary, opening paragraph), i.e. b / (c*G) bits per element (0.5 at
+ * c=4, G=4, b=8; 0.25 at c=8).  The first P prefix and last R recent tokens
+ * of every sequence stay bf16 (airadar.tv summary, section "Utilisation").
+ * The serving path stores the indices packed and decodes with fused kernels
+ * (airadar.tv summary, section "Raisons"); this library is that path.
+ *
+ * Conventions for every entry point
+ *   - All sizes are element counts unless a name ends in _bytes.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Device pointers are HIP device addresses of memory the CALLER owns; the
+ *     library never allocates, frees or synchronises, and keeps no state other
+ *     than a thread-local error string.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Launches are
+ *     asynchronous; faults inside a kernel surface at the caller's next
+ *     synchronisation on that stream.
+ *   - Every host-detectable problem (bad configuration, NULL or misaligned
+ *     pointer, unsupported variant, small workspace) returns a negative status
+ *     BEFORE any HIP call, with no partial work; loopvq_last_error() then holds a
+ *     description.  A failed launch returns LOOPVQ_ERR_HIP.
+ *   - Calls are reentrant; two calls that write the same buffers race.
+ */
+#ifndef LOOPVQ_H
+#define LOOPVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t loopvq_status;
+#define LOOPVQ_OK 0
+#define LOOPVQ_ERR_INVALID_ARG (-1)
+#define LOOPVQ_ERR_UNSUPPORTED (-2)
+#define LOOPVQ_ERR_MISALIGNED (-3)
+#define LOOPVQ_ERR_WORKSPACE (-4)
+#define LOOPVQ_ERR_HIP (-5)
+
+/* Model / cache shape.  All fields int32.
+ *   num_layers L, num_loops T, loop_group G (T % G == 0: a loop group is the
+ *   G consecutive loop steps [j*G, j*G+G) sharing one index, J = T/G groups);
+ *   num_q_heads Hq, num_kv_heads Hkv (Hq % Hkv == 0), head_dim d,
+ *   chans_per_group c (d % c == 0, NG = d/c channel groups, NG % 4 == 0),
+ *   index_bits b in [1,16] (K = 2^b codewords), prefix_tokens P and
+ *   recent_tokens R (bf16 windows), page_tokens PT (tokens per index page, a
+ *   power of two >= 64), codebook_per_loop_group (0: one codebook set per
+ *   (layer, kv-head, group) shared by all loop groups, Jcb = 1; 1: one per loop
+ *   group, Jcb = J).
+ * Kernels are built for b = 8, (c, G) in {(4,4), (8,4)}, NG in {16, 32}; other
+ * valid shapes return LOOPVQ_ERR_UNSUPPORTED from encode / decode. */
+typedef struct loopvq_config {
+  int32_t num_layers;
+  int32_t num_loops;
+  int32_t loop_group;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t chans_per_group;
+  int32_t index_bits;
+  int32_t prefix_tokens;
+  int32_t recent_tokens;
+  int32_t page_tokens;
+  int32_t codebook_per_loop_group;
+} loopvq_config;
+
+/* Byte sizes and strides of every buffer the library reads or writes.
+ *
+ * Index pool (uint8): [L][J][Hkv][num_pages][page_bytes].  A page holds the
+ * packed indices of PT consecutive vector-quantized positions of one
+ * (layer, loop group, kv-head): [kind: K then V][PT/4 token quads][NG/4 group
+ * quads][micro-tile of 2*b bytes].  A micro-tile packs 16 indices: element
+ * e = 4*i + r is token 4*Q + i, group 4*u + r; bit beta of element e sits at
+ * bit e*b + beta of the tile read as a little-endian integer.  Unwritten
+ * slots must be zero (zero the pool before the first encode).
+ * A block table int32 [B][max_pages_per_seq] maps (sequence, vq_position/PT)
+ * to a page index; vq_position u of token n is n - P.
+ *
+ * Canonical codebooks (bf16): [L][Jcb][Hkv][NG][K][c*G]; row k of group g is a
+ * sub-vector in loop-major order (element tau*c + i = channel g*c + i of loop
+ * step tau of the group).  K and V have separate codebooks.
+ * Prepared codebooks (bf16, written by loopvq_codebook_prepare):
+ * [L][Jcb][Hkv][G][K][d], so the loop-step-tau slice of a codebook set is one
+ * contiguous K x d block; norms (fp32): [L][Jcb][Hkv][NG][K] squared norms.
+ * Windows (bf16) for one (layer, loop step): prefix [B][Hkv][P][d], recent
+ * [B][Hkv][R][d]; rows [0, n_prefix) and [0, n_recent) are read. */
+typedef struct loopvq_layout {
+  int64_t tile_bytes;
+  int64_t kind_bytes;
+  int64_t page_bytes;
+  int64_t pool_head_stride_bytes; /* num_pages * page_bytes */
+  int64_t pool_bytes;             /* L * J * Hkv * num_pages * page_bytes */
+  int64_t codebook_elems;         /* bf16 elements of one canonical (or prepared) codebook set, K or V */
+  int64_t norms_elems;            /* fp32 elements of one norms array */
+  int64_t prefix_elems;           /* bf16 elements of one prefix window buffer, for one (l, t) */
+  int64_t recent_elems;           /* bf16 elements of one recent window buffer, for one (l, t) */
+  double bits_per_elem;           /* b / (c*G) */
+} loopvq_layout;
+
+/* Validate a configuration: the rules above (ranges, divisibility, page size).
+ * Returns LOOPVQ_OK or LOOPVQ_ERR_INVALID_ARG; never touches the GPU. */
+loopvq_status loopvq_config_check(const loopvq_config* cfg);
+
+/* Index bits per cache element, b / (c*G) (0.5 and 0.25 are the operating
+ * points in the arXiv 2611.05304 abstract).  Returns -1.0 for an invalid config. */
+double loopvq_bits_per_elem(const loopvq_config* cfg);
+
+/* Fill *out with the sizes above for `batch` sequences and a pool of
+ * `num_pages` pages per (layer, loop group, kv-head).  Host only. */
+loopvq_status loopvq_layout_query(const loopvq_config* cfg, int32_t batch, int64_t num_pages,
+                                  loopvq_layout* out);
+
+/* Derive the decode-side codebook copies from canonical codebooks.
+ *   cb        device, bf16 canonical [L][Jcb][Hkv][NG][K][c*G] (one kind)
+ *   cb_prep   device, bf16 prepared  [L][Jcb][Hkv][G][K][d]   (written)
+ *   cb_norms  device, fp32 [L][Jcb][Hkv][NG][K] squared norms (written; may be NULL)
+ * Pointers 16-byte aligned.  Run once per codebook set, off the per-token path. */
+loopvq_status loopvq_codebook_prepare(const loopvq_config* cfg, const uint16_t* cb,
+                                      uint16_t* cb_prep, float* cb_norms, void* stream);
+
+/* Encode: nearest codeword (plain squared Euclidean distance, lowest index on
+ * ties) of every sub-vector of n_tokens token rows, for every kv-head and
+ * channel group of one (layer, loop group, kind), packed into the pool.
+ * Sub-vector (row r, head h, group g) element tau*c + i is
+ *   src[tau*stride_loop + r*stride_token + h*stride_head + g*c + i],  tau < G.
+ * Distances are screened on bf16 matrix cores in fp32; whenever the two best
+ * screened distances are within the screen's rounding bound, every codeword is
+ * re-scored exactly in fp64, so the result equals a brute-force fp64 search. */
+typedef struct loopvq_encode_args {
+  int32_t layer;                /* l in [0, L) */
+  int32_t loop_group;           /* j in [0, J) */
+  int32_t kind;                 /* 0 = keys, 1 = values */
+  int32_t n_tokens;             /* rows to encode (>= 0) */
+  const uint16_t* src;          /* device bf16; 16-byte aligned; rows 16-byte aligned */
+  int64_t stride_loop;          /* elements between loop steps tau and tau+1 */
+  int64_t stride_token;         /* elements between rows r and r+1 */
+  int64_t stride_head;          /* elements between kv-heads */
+  const int32_t* seq_id;        /* device [n_tokens]: sequence of each row, in [0, batch) */
+  const int32_t* vq_pos;        /* device [n_tokens]: vq position u of each row, u >= 0 */
+  const int32_t* block_table;   /* device [batch][max_pages_per_seq] */
+  int32_t batch;
+  int32_t max_pages_per_seq;
+  int64_t num_pages;            /* pages per (layer, loop group, kv-head) in the pool */
+  const uint16_t* cb;           /* device canonical codebooks of this kind, bf16 */
+  const float* cb_norms;        /* device squared norms of this kind (loopvq_codebook_prepare) */
+  uint8_t* pool;                /* device index pool (written) */
+  int32_t* out_idx;             /* optional device [n_tokens][Hkv][NG] copy of the chosen indices */
+  unsigned long long* rerank_count; /* optional device counter: += sub-vectors re-scored in fp64 */
+} loopvq_encode_args;
+
+loopvq_status loopvq_encode(const loopvq_config* cfg, const loopvq_encode_args* args, void* stream);
+
+/* Decode attention for one (layer l, loop step t) over all B sequences and Hq
+ * query heads: for query (b, hq) with kv-head h = hq / (Hq/Hkv) and N =
+ * seq_lens[b] cached tokens (the token being decoded included), the keys and
+ * values are [prefix rows | vector-quantized rows | recent rows] with
+ * n_prefix = min(P, N), n_vq = max(0, N - P - R), n_recent = N - n_prefix - n_vq;
+ * a VQ row's channels [g*c, g*c+c) are the loop-step-(t mod G) slice of
+ * codeword idx[g] of the (l, t/G) pages.  Output
+ *   out[b][hq][:] = sum_n softmax_n(scale * q'.k_n) v_n  (fp32),
+ *   lse[b][hq]    = ln sum_n exp(scale * q'.k_n),
+ * with q' = R^T q when `rot` (fp32 [d][d] row-major, R[i][j]) is given, else q.
+ * The kernel builds a q.codeword lookup table per channel group in LDS, reads
+ * the packed indices once, and accumulates V as codeword-index histograms.
+ * Tokens are split across workgroups (num_splits, 0 = automatic); splits are
+ * merged with log-sum-exp in a second kernel using `workspace`. */
+typedef struct loopvq_decode_args {
+  int32_t layer;                /* l in [0, L) */
+  int32_t loop;                 /* t in [0, T) */
+  int32_t batch;                /* B > 0 */
+  int32_t max_pages_per_seq;
+  int32_t max_seq_len;          /* upper bound of seq_lens[] (sizes the split plan) */
+  int32_t num_splits;           /* 0 = automatic, else 1..256 */
+  int64_t num_pages;            /* pages per (layer, loop group, kv-head) */
+  const uint16_t* q;            /* device bf16 [B][Hq][d] */
+  const int32_t* seq_lens;      /* device [B], each in [1, max_seq_len] */
+  const int32_t* block_table;   /* device [B][max_pages_per_seq] */
+  const uint8_t* pool;          /* device index pool */
+  const uint16_t* cb_k_prep;    /* device prepared key codebooks */
+  const uint16_t* cb_v_prep;    /* device prepared value codebooks */
+  const uint16_t* k_prefix;     /* device bf16 [B][Hkv][P][d] for (l, t); NULL allowed iff P == 0 */
+  const uint16_t* v_prefix;
+  const uint16_t* k_recent;     /* device bf16 [B][Hkv][R][d] for (l, t); NULL allowed iff R == 0 */
+  const uint16_t* v_recent;
+  const float* rot;             /* device fp32 [d][d] or NULL */
+  float softmax_scale;          /* <= 0 selects 1/sqrt(d) */
+  float* out;                   /* device fp32 [B][Hq][d] (written) */
+  float* lse;                   /* device fp32 [B][Hq] or NULL */
+} loopvq_decode_args;
+
+/* Workspace bytes loopvq_decode_attn needs for this batch and maximum length
+ * (the automatic split plan; explicit num_splits needs <= 256 * B*Hq*(d+4)*4). */
+loopvq_status loopvq_decode_attn_workspace(const loopvq_config* cfg, int32_t batch,
+                                           int32_t max_seq_len, size_t* bytes);
+
+loopvq_status loopvq_decode_attn(const loopvq_config* cfg, const loopvq_decode_args* args,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* loopvq_status_string(loopvq_status s);
+
+/* Detail of the last error on this thread ("" if none). */
+const char* loopvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LOOPVQ_H */

@@ -1,0 +1,329 @@
+// C ABI of the LoopVQ library: argument validation, layout arithmetic, split planning
+// and kernel launches.  Every check runs before any HIP call, so a rejected call has
+// no side effect; the only state is a thread-local error string.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/loopvq.h"
+#include "lvq_common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+loopvq_status fail(loopvq_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+loopvq_status ok() {
+  g_err[0] = '\0';
+  return LOOPVQ_OK;
+}
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int ilog2(int64_t v) {
+  int r = 0;
+  while ((int64_t(1) << r) < v) ++r;
+  return r;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+loopvq_status check_config(const loopvq_config* c) {
+  if (!c) return fail(LOOPVQ_ERR_INVALID_ARG, "config is NULL");
+  if (c->num_layers < 1 || c->num_loops < 1 || c->loop_group < 1)
+    return fail(LOOPVQ_ERR_INVALID_ARG, "num_layers, num_loops and loop_group must be >= 1");
+  if (c->num_loops % c->loop_group)
+    return fail(LOOPVQ_ERR_INVALID_ARG, "num_loops (%d) must be a multiple of loop_group (%d)", c->num_loops,
+                c->loop_group);
+  if (c->num_q_heads < 1 || c->num_kv_heads < 1 || c->num_q_heads % c->num_kv_heads)
+    return fail(LOOPVQ_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+  if (c->head_dim < 1 || c->chans_per_group < 1 || c->head_dim % c->chans_per_group)
+    return fail(LOOPVQ_ERR_INVALID_ARG, "head_dim must be a positive multiple of chans_per_group");
+  if ((c->head_dim / c->chans_per_group) % 4)
+    return fail(LOOPVQ_ERR_INVALID_ARG, "head_dim / chans_per_group must be a multiple of 4");
+  if (c->index_bits < 1 || c->index_bits > 16) return fail(LOOPVQ_ERR_INVALID_ARG, "index_bits must be in [1, 16]");
+  if (c->prefix_tokens < 0 || c->recent_tokens < 0)
+    return fail(LOOPVQ_ERR_INVALID_ARG, "prefix_tokens and recent_tokens must be >= 0");
+  if (c->page_tokens < 64 || !is_pow2(c->page_tokens))
+    return fail(LOOPVQ_ERR_INVALID_ARG, "page_tokens must be a power of two >= 64");
+  if (c->codebook_per_loop_group != 0 && c->codebook_per_loop_group != 1)
+    return fail(LOOPVQ_ERR_INVALID_ARG, "codebook_per_loop_group must be 0 or 1");
+  return LOOPVQ_OK;
+}
+
+// Variants the kernels are built for.
+loopvq_status check_supported(const loopvq_config* c) {
+  const int ng = c->head_dim / c->chans_per_group;
+  if (c->index_bits != 8) return fail(LOOPVQ_ERR_UNSUPPORTED, "kernels are built for index_bits = 8 only");
+  if (c->loop_group != 4) return fail(LOOPVQ_ERR_UNSUPPORTED, "kernels are built for loop_group = 4 only");
+  const bool okv = (c->chans_per_group == 4 && (ng == 16 || ng == 32)) || (c->chans_per_group == 8 && ng == 16);
+  if (!okv)
+    return fail(LOOPVQ_ERR_UNSUPPORTED, "kernels are built for (c, d) in {(4, 64), (4, 128), (8, 128)}; got (%d, %d)",
+                c->chans_per_group, c->head_dim);
+  return LOOPVQ_OK;
+}
+
+struct Sizes {
+  int ng, J, Jcb, K, E;
+  int64_t tile_bytes, kind_bytes, page_bytes;
+};
+
+Sizes sizes_of(const loopvq_config* c) {
+  Sizes s;
+  s.ng = c->head_dim / c->chans_per_group;
+  s.J = c->num_loops / c->loop_group;
+  s.Jcb = c->codebook_per_loop_group ? s.J : 1;
+  s.K = 1 << c->index_bits;
+  s.E = c->chans_per_group * c->loop_group;
+  s.tile_bytes = 2 * int64_t(c->index_bits);
+  s.kind_bytes = int64_t(c->page_tokens / 4) * (s.ng / 4) * s.tile_bytes;
+  s.page_bytes = 2 * s.kind_bytes;
+  return s;
+}
+
+// Tokens per wave tile of the decode kernel (1 KB of 8-bit indices).
+int decode_tile_tokens(const loopvq_config* c) { return 256 / ((c->head_dim / c->chans_per_group) / 4); }
+
+int plan_splits(const loopvq_config* c, int32_t batch, int32_t max_seq_len) {
+  const int64_t Q = int64_t(batch) * c->num_q_heads;
+  const int64_t n_vq = std::max<int64_t>(0, int64_t(max_seq_len) - c->prefix_tokens - c->recent_tokens);
+  const int64_t tiles = (n_vq + decode_tile_tokens(c) - 1) / decode_tile_tokens(c);
+  const int64_t slots = 512;  // 256 CUs x 2 resident workgroups
+  int64_t S = Q >= slots ? 1 : (slots + Q - 1) / Q;
+  const int64_t max_by_work = std::max<int64_t>(1, tiles / 16);   // >= 16 tiles per split
+  S = std::min(S, max_by_work);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(S, 256));
+}
+
+}  // namespace
+
+extern "C" {
+
+loopvq_status loopvq_config_check(const loopvq_config* cfg) {
+  const loopvq_status s = check_config(cfg);
+  return s == LOOPVQ_OK ? ok() : s;
+}
+
+double loopvq_bits_per_elem(const loopvq_config* cfg) {
+  if (check_config(cfg) != LOOPVQ_OK) return -1.0;
+  return double(cfg->index_bits) / double(cfg->chans_per_group * cfg->loop_group);
+}
+
+loopvq_status loopvq_layout_query(const loopvq_config* cfg, int32_t batch, int64_t num_pages, loopvq_layout* out) {
+  loopvq_status s = check_config(cfg);
+  if (s) return s;
+  if (!out) return fail(LOOPVQ_ERR_INVALID_ARG, "out is NULL");
+  if (batch < 1) return fail(LOOPVQ_ERR_INVALID_ARG, "batch must be >= 1");
+  if (num_pages < 1) return fail(LOOPVQ_ERR_INVALID_ARG, "num_pages must be >= 1");
+  const Sizes z = sizes_of(cfg);
+  out->tile_bytes = z.tile_bytes;
+  out->kind_bytes = z.kind_bytes;
+  out->page_bytes = z.page_bytes;
+  out->pool_head_stride_bytes = num_pages * z.page_bytes;
+  out->pool_bytes = int64_t(cfg->num_layers) * z.J * cfg->num_kv_heads * out->pool_head_stride_bytes;
+  out->codebook_elems = int64_t(cfg->num_layers) * z.Jcb * cfg->num_kv_heads * z.ng * z.K * z.E;
+  out->norms_elems = int64_t(cfg->num_layers) * z.Jcb * cfg->num_kv_heads * z.ng * z.K;
+  out->prefix_elems = int64_t(batch) * cfg->num_kv_heads * cfg->prefix_tokens * cfg->head_dim;
+  out->recent_elems = int64_t(batch) * cfg->num_kv_heads * cfg->recent_tokens * cfg->head_dim;
+  out->bits_per_elem = double(cfg->index_bits) / double(cfg->chans_per_group * cfg->loop_group);
+  return ok();
+}
+
+loopvq_status loopvq_codebook_prepare(const loopvq_config* cfg, const uint16_t* cb, uint16_t* cb_prep,
+                                      float* cb_norms, void* stream) {
+  loopvq_status s = check_config(cfg);
+  if (s) return s;
+  if (!cb || !cb_prep) return fail(LOOPVQ_ERR_INVALID_ARG, "cb and cb_prep must not be NULL");
+  if (!aligned(cb, 16) || !aligned(cb_prep, 16) || (cb_norms && !aligned(cb_norms, 16)))
+    return fail(LOOPVQ_ERR_MISALIGNED, "codebook pointers must be 16-byte aligned");
+  const Sizes z = sizes_of(cfg);
+  lvq::PrepareParams p{};
+  p.sets = int64_t(cfg->num_layers) * z.Jcb * cfg->num_kv_heads;
+  p.NG = z.ng;
+  p.K = z.K;
+  p.c = cfg->chans_per_group;
+  p.G = cfg->loop_group;
+  p.d = cfg->head_dim;
+  p.cb = cb;
+  p.prep = cb_prep;
+  p.norms = cb_norms;
+  const hipError_t e = lvq::launch_prepare(p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LOOPVQ_ERR_HIP, "codebook_prepare launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+loopvq_status loopvq_encode(const loopvq_config* cfg, const loopvq_encode_args* a, void* stream) {
+  loopvq_status s = check_config(cfg);
+  if (s) return s;
+  if (!a) return fail(LOOPVQ_ERR_INVALID_ARG, "args is NULL");
+  if ((s = check_supported(cfg))) return s;
+  const Sizes z = sizes_of(cfg);
+  if (a->layer < 0 || a->layer >= cfg->num_layers) return fail(LOOPVQ_ERR_INVALID_ARG, "layer out of range");
+  if (a->loop_group < 0 || a->loop_group >= z.J) return fail(LOOPVQ_ERR_INVALID_ARG, "loop_group out of range");
+  if (a->kind != 0 && a->kind != 1) return fail(LOOPVQ_ERR_INVALID_ARG, "kind must be 0 (K) or 1 (V)");
+  if (a->n_tokens < 0) return fail(LOOPVQ_ERR_INVALID_ARG, "n_tokens must be >= 0");
+  if (a->batch < 1 || a->max_pages_per_seq < 1 || a->num_pages < 1)
+    return fail(LOOPVQ_ERR_INVALID_ARG, "batch, max_pages_per_seq and num_pages must be >= 1");
+  if (!a->src || !a->seq_id || !a->vq_pos || !a->block_table || !a->cb || !a->cb_norms || !a->pool)
+    return fail(LOOPVQ_ERR_INVALID_ARG, "src, seq_id, vq_pos, block_table, cb, cb_norms and pool must not be NULL");
+  const int vec = cfg->chans_per_group;  // elements per aligned load (8 B at c=4, 16 B at c=8)
+  if (!aligned(a->src, 2 * vec) || a->stride_loop % vec || a->stride_token % vec || a->stride_head % vec)
+    return fail(LOOPVQ_ERR_MISALIGNED, "src must be %d-byte aligned and its strides multiples of %d elements",
+                2 * vec, vec);
+  if (!aligned(a->cb, 16) || !aligned(a->cb_norms, 16))
+    return fail(LOOPVQ_ERR_MISALIGNED, "cb and cb_norms must be 16-byte aligned");
+  if (a->out_idx && !aligned(a->out_idx, 4)) return fail(LOOPVQ_ERR_MISALIGNED, "out_idx must be 4-byte aligned");
+  if (a->rerank_count && !aligned(a->rerank_count, 8))
+    return fail(LOOPVQ_ERR_MISALIGNED, "rerank_count must be 8-byte aligned");
+  const int jcb = cfg->codebook_per_loop_group ? a->loop_group : 0;
+  lvq::EncodeParams p{};
+  p.n_tokens = a->n_tokens;
+  p.Hkv = cfg->num_kv_heads;
+  p.NG = z.ng;
+  p.G = cfg->loop_group;
+  p.pt_shift = ilog2(cfg->page_tokens);
+  p.max_pages = a->max_pages_per_seq;
+  p.batch = a->batch;
+  p.kind = a->kind;
+  p.num_pages = a->num_pages;
+  p.page_bytes = z.page_bytes;
+  p.kind_bytes = z.kind_bytes;
+  p.head_stride = a->num_pages * z.page_bytes;
+  p.src = a->src;
+  p.stride_loop = a->stride_loop;
+  p.stride_token = a->stride_token;
+  p.stride_head = a->stride_head;
+  p.seq_id = a->seq_id;
+  p.vq_pos = a->vq_pos;
+  p.block_table = a->block_table;
+  const int64_t set0 = (int64_t(a->layer) * z.Jcb + jcb) * cfg->num_kv_heads;
+  p.cb_lj = a->cb + set0 * z.ng * z.K * z.E;
+  p.norms_lj = a->cb_norms + set0 * z.ng * z.K;
+  p.pool_lj = a->pool + (int64_t(a->layer) * z.J + a->loop_group) * cfg->num_kv_heads * p.head_stride;
+  p.out_idx = a->out_idx;
+  p.rerank_count = a->rerank_count;
+  const hipError_t e = lvq::launch_encode(p, cfg->chans_per_group, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LOOPVQ_ERR_HIP, "encode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+loopvq_status loopvq_decode_attn_workspace(const loopvq_config* cfg, int32_t batch, int32_t max_seq_len,
+                                           size_t* bytes) {
+  loopvq_status s = check_config(cfg);
+  if (s) return s;
+  if (!bytes) return fail(LOOPVQ_ERR_INVALID_ARG, "bytes is NULL");
+  if (batch < 1 || max_seq_len < 1) return fail(LOOPVQ_ERR_INVALID_ARG, "batch and max_seq_len must be >= 1");
+  const int S = plan_splits(cfg, batch, max_seq_len);
+  *bytes = S > 1 ? size_t(S) * batch * cfg->num_q_heads * (cfg->head_dim + 4) * sizeof(float) : 0;
+  return ok();
+}
+
+loopvq_status loopvq_decode_attn(const loopvq_config* cfg, const loopvq_decode_args* a, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  loopvq_status s = check_config(cfg);
+  if (s) return s;
+  if (!a) return fail(LOOPVQ_ERR_INVALID_ARG, "args is NULL");
+  if ((s = check_supported(cfg))) return s;
+  const Sizes z = sizes_of(cfg);
+  if (a->layer < 0 || a->layer >= cfg->num_layers) return fail(LOOPVQ_ERR_INVALID_ARG, "layer out of range");
+  if (a->loop < 0 || a->loop >= cfg->num_loops) return fail(LOOPVQ_ERR_INVALID_ARG, "loop out of range");
+  if (a->batch < 1) return fail(LOOPVQ_ERR_INVALID_ARG, "batch must be >= 1");
+  if (a->max_seq_len < 1) return fail(LOOPVQ_ERR_INVALID_ARG, "max_seq_len must be >= 1");
+  if (a->num_splits < 0 || a->num_splits > 256) return fail(LOOPVQ_ERR_INVALID_ARG, "num_splits must be in [0, 256]");
+  if (int64_t(a->batch) * cfg->num_q_heads * 256 > (int64_t(1) << 31) - 1)
+    return fail(LOOPVQ_ERR_INVALID_ARG, "batch * num_q_heads too large");
+  if (!a->q || !a->seq_lens || !a->out) return fail(LOOPVQ_ERR_INVALID_ARG, "q, seq_lens and out must not be NULL");
+  const bool can_vq = int64_t(a->max_seq_len) > int64_t(cfg->prefix_tokens) + cfg->recent_tokens;
+  if (can_vq) {
+    if (!a->block_table || !a->pool || !a->cb_k_prep || !a->cb_v_prep)
+      return fail(LOOPVQ_ERR_INVALID_ARG, "block_table, pool and prepared codebooks must not be NULL");
+    if (a->max_pages_per_seq < 1 || a->num_pages < 1)
+      return fail(LOOPVQ_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
+    if (!aligned(a->pool, 16) || !aligned(a->cb_k_prep, 16) || !aligned(a->cb_v_prep, 16))
+      return fail(LOOPVQ_ERR_MISALIGNED, "pool and prepared codebooks must be 16-byte aligned");
+  }
+  if (cfg->prefix_tokens > 0 && (!a->k_prefix || !a->v_prefix))
+    return fail(LOOPVQ_ERR_INVALID_ARG, "prefix windows must not be NULL when prefix_tokens > 0");
+  if (cfg->recent_tokens > 0 && (!a->k_recent || !a->v_recent))
+    return fail(LOOPVQ_ERR_INVALID_ARG, "recent windows must not be NULL when recent_tokens > 0");
+  if ((a->k_prefix && !aligned(a->k_prefix, 16)) || (a->v_prefix && !aligned(a->v_prefix, 16)) ||
+      (a->k_recent && !aligned(a->k_recent, 16)) || (a->v_recent && !aligned(a->v_recent, 16)))
+    return fail(LOOPVQ_ERR_MISALIGNED, "window buffers must be 16-byte aligned");
+  if (!aligned(a->q, 2) || !aligned(a->out, 4) || (a->lse && !aligned(a->lse, 4)) || (a->rot && !aligned(a->rot, 4)) ||
+      !aligned(a->seq_lens, 4))
+    return fail(LOOPVQ_ERR_MISALIGNED, "q, out, lse, rot or seq_lens misaligned");
+  const int S = a->num_splits > 0 ? a->num_splits : plan_splits(cfg, a->batch, a->max_seq_len);
+  const int64_t Q = int64_t(a->batch) * cfg->num_q_heads;
+  const size_t need = S > 1 ? size_t(S) * Q * (cfg->head_dim + 4) * sizeof(float) : 0;
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(LOOPVQ_ERR_WORKSPACE, "workspace too small: %zu bytes needed for %d splits", need, S);
+  if (need && !aligned(workspace, 16)) return fail(LOOPVQ_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+
+  const int j = a->loop / cfg->loop_group;
+  const int jcb = cfg->codebook_per_loop_group ? j : 0;
+  lvq::DecodeParams p{};
+  p.B = a->batch;
+  p.Hq = cfg->num_q_heads;
+  p.Hkv = cfg->num_kv_heads;
+  p.d = cfg->head_dim;
+  p.P = cfg->prefix_tokens;
+  p.R = cfg->recent_tokens;
+  p.G = cfg->loop_group;
+  p.pt_shift = ilog2(cfg->page_tokens);
+  p.max_pages = can_vq ? a->max_pages_per_seq : 0;
+  p.max_seq_len = a->max_seq_len;
+  p.S = S;
+  p.tau = a->loop % cfg->loop_group;
+  p.num_pages = a->num_pages;
+  p.page_bytes = z.page_bytes;
+  p.kind_bytes = z.kind_bytes;
+  const float scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / std::sqrt(float(cfg->head_dim));
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.q = a->q;
+  p.seq_lens = a->seq_lens;
+  p.block_table = a->block_table;
+  p.head_stride = a->num_pages * z.page_bytes;
+  p.pool_lj = can_vq ? a->pool + (int64_t(a->layer) * z.J + j) * cfg->num_kv_heads * p.head_stride : nullptr;
+  const int64_t set0 = (int64_t(a->layer) * z.Jcb + jcb) * cfg->num_kv_heads;
+  const int64_t set_elems = int64_t(cfg->loop_group) * z.K * cfg->head_dim;
+  p.cbk = can_vq ? a->cb_k_prep + set0 * set_elems : nullptr;
+  p.cbv = can_vq ? a->cb_v_prep + set0 * set_elems : nullptr;
+  p.k_prefix = a->k_prefix;
+  p.v_prefix = a->v_prefix;
+  p.k_recent = a->k_recent;
+  p.v_recent = a->v_recent;
+  p.rot = a->rot;
+  p.out = a->out;
+  p.lse = a->lse;
+  p.ws = static_cast<float*>(workspace);
+  const hipError_t e = lvq::launch_decode(p, z.ng, cfg->chans_per_group, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LOOPVQ_ERR_HIP, "decode_attn launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* loopvq_status_string(loopvq_status s) {
+  switch (s) {
+    case LOOPVQ_OK: return "ok";
+    case LOOPVQ_ERR_INVALID_ARG: return "invalid argument";
+    case LOOPVQ_ERR_UNSUPPORTED: return "unsupported variant";
+    case LOOPVQ_ERR_MISALIGNED: return "misaligned pointer";
+    case LOOPVQ_ERR_WORKSPACE: return "workspace too small";
+    case LOOPVQ_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* loopvq_last_error(void) { return g_err; }
+
+}  // extern "C"

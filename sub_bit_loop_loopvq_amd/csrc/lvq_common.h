@@ -1,0 +1,99 @@
+// Shared definitions of the LoopVQ HIP library: launch parameter blocks and
+// small device helpers (bf16 conversion, DPP lane exchanges).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lvq {
+
+constexpr int kCodes = 256;     // K = 2^b for the built variant b = 8
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Parameter blocks (host fills, kernels read; passed by value)
+// ---------------------------------------------------------------------------
+struct DecodeParams {
+  int B, Hq, Hkv, d, P, R, G;
+  int pt_shift;              // log2(page_tokens)
+  int max_pages;             // block-table row stride
+  int max_seq_len;
+  int S;                     // splits per query
+  int tau;                   // loop step within its group (t mod G)
+  int64_t num_pages, page_bytes, kind_bytes;
+  float scale_log2;          // softmax scale * log2(e)
+  const uint16_t* q;         // [B][Hq][d]
+  const int32_t* seq_lens;   // [B]
+  const int32_t* block_table;
+  const uint8_t* pool_lj;    // pool + ((l*J + j)*Hkv) * head_stride
+  int64_t head_stride;       // num_pages * page_bytes
+  const uint16_t* cbk;       // prepared key codebooks of (l, jcb): [Hkv][G][K][d]
+  const uint16_t* cbv;       // prepared value codebooks of (l, jcb)
+  const uint16_t* k_prefix;  // [B][Hkv][P][d]
+  const uint16_t* v_prefix;
+  const uint16_t* k_recent;  // [B][Hkv][R][d]
+  const uint16_t* v_recent;
+  const float* rot;          // [d][d] or nullptr
+  float* out;                // [B][Hq][d]
+  float* lse;                // [B][Hq] or nullptr
+  float* ws;                 // partials [S][B*Hq][d + 4] when S > 1
+};
+
+struct EncodeParams {
+  int n_tokens, Hkv, NG, G, pt_shift, max_pages, batch, kind;
+  int64_t num_pages, page_bytes, kind_bytes, head_stride;
+  const uint16_t* src;
+  int64_t stride_loop, stride_token, stride_head;
+  const int32_t* seq_id;
+  const int32_t* vq_pos;
+  const int32_t* block_table;
+  const uint16_t* cb_lj;     // canonical codebooks of (l, jcb): [Hkv][NG][K][E]
+  const float* norms_lj;     // [Hkv][NG][K]
+  uint8_t* pool_lj;          // pool + ((l*J + j)*Hkv) * head_stride
+  int32_t* out_idx;
+  unsigned long long* rerank_count;
+};
+
+struct PrepareParams {
+  int64_t sets;              // L * Jcb * Hkv codebook sets
+  int NG, K, c, G, d;
+  const uint16_t* cb;
+  uint16_t* prep;
+  float* norms;
+};
+
+// Launchers (defined next to their kernels).  Return hipSuccess or the launch error.
+hipError_t launch_decode(const DecodeParams& p, int ng, int c, hipStream_t stream);
+hipError_t launch_encode(const EncodeParams& p, int c, hipStream_t stream);
+hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_at(const uint16_t* p) { return __uint_as_float(uint32_t(*p) << 16); }
+
+// DPP controls (GCN/CDNA encoding)
+constexpr int dpp_quad(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
+constexpr int kDppRowHalfMirror = 0x141;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+}  // namespace lvq

@@ -209,19 +209,19 @@ def codebook_tokens(wl: Workload, kind: int, l: int, h: int,
     return to_bf16_bits(v)
 
 
-def codebooks(wl: Workload, kind: int, sc: np.ndarray | None = None) -> np.ndarray:
+def codebooks(wl: Workload, kind: int, sc: np.ndarray | None = None, layers=None) -> np.ndarray:
     """bf16 bits [L][Jcb][Hkv][d/c][K][c*G]: codebook rows in the library's input format.
 
     Row k of (layer l, codebook loop group jc, head h, group g) is fresh token k's
     channels [g*c, g*c + c) over loop steps jc*G .. jc*G + G - 1, loop-major
-    (element tau*c + i).
+    (element tau*c + i).  With ``layers`` given, only those layers are filled (the rest stay zero).
     """
     if sc is None:
         sc = scales(wl)
     L, Jc, H, NG, K, c, G = (wl.layers, wl.cb_loop_groups, wl.kv_heads, wl.groups,
                              wl.codewords, wl.chans, wl.loop_group)
-    out = np.empty((L, Jc, H, NG, K, c * G), dtype=np.uint16)
-    for l in range(L):
+    out = np.zeros((L, Jc, H, NG, K, c * G), dtype=np.uint16)
+    for l in (range(L) if layers is None else layers):
         for h in range(H):
             tok = codebook_tokens(wl, kind, l, h, sc)          # [K][T][d]
             for jc in range(Jc):

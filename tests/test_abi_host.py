@@ -1,0 +1,200 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared entry point,
+and rejects bad calls on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sub_bit_loop_loopvq_amd as lvq
+from oracle import loopvq_oracle as O
+from synth import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_entry_points():
+    text = open(os.path.join(ROOT, "include", "loopvq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(loopvq_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_entry_points()
+    assert set(names) == set(lvq.EXPORTS)
+    L = lvq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    # symbols are plain C (unmangled) exports
+    raw = ctypes.CDLL(lvq.LIB_PATH)
+    for n in names:
+        ctypes.cast(getattr(raw, n), ctypes.c_void_p)
+
+
+def test_struct_sizes_match_header_layout():
+    # int32 x12 config; layout 9 int64 + 1 double
+    assert ctypes.sizeof(lvq.loopvq_config) == 48
+    assert ctypes.sizeof(lvq.loopvq_layout) == 80
+    assert ctypes.sizeof(lvq.loopvq_encode_args) == 4 * 4 + 8 + 3 * 8 + 3 * 8 + 4 + 4 + 8 + 5 * 8
+    assert ctypes.sizeof(lvq.loopvq_decode_args) == 6 * 4 + 8 + 10 * 8 + 8 + 8 + 8 + 8
+
+
+@pytest.mark.parametrize("wl", W.ALL, ids=[w.name for w in W.ALL])
+def test_config_check_and_bits_per_elem(wl):
+    cfg = lvq.make_config(wl)
+    assert lvq.loopvq_config_check(cfg) == 0
+    assert lvq.loopvq_bits_per_elem(cfg) == O.bits_per_elem(wl.index_bits, wl.chans, wl.loop_group)
+
+
+def test_config_rules_agree_with_oracle():
+    base = dict(T=4, G=4, Hq=16, Hkv=16, d=128, c=4, b=8)
+    for bad in [{}, dict(T=6), dict(d=130), dict(Hq=3, Hkv=2), dict(b=17), dict(b=0), dict(d=24, c=4),
+                dict(c=8), dict(c=2, d=64), dict(G=2), dict(Hq=32)]:
+        kw = dict(base, **bad)
+        try:
+            O.check_config(**kw)
+            oracle_ok = True
+        except ValueError:
+            oracle_ok = False
+        cfg = lvq.make_config(num_layers=1, num_loops=kw["T"], loop_group=kw["G"], num_q_heads=kw["Hq"],
+                              num_kv_heads=kw["Hkv"], head_dim=kw["d"], chans_per_group=kw["c"],
+                              index_bits=kw["b"], prefix_tokens=8, recent_tokens=64, page_tokens=64,
+                              codebook_per_loop_group=0)
+        assert (lvq.loopvq_config_check(cfg) == 0) == oracle_ok, kw
+
+
+def test_config_rejections_and_messages():
+    good = lvq.make_config(W.STACK_32K)
+    for field, val in [("num_loops", 6), ("page_tokens", 96), ("page_tokens", 32), ("prefix_tokens", -1),
+                       ("codebook_per_loop_group", 2), ("num_layers", 0), ("index_bits", 0)]:
+        cfg = lvq.make_config(W.STACK_32K)
+        setattr(cfg, field, val)
+        assert lvq.loopvq_config_check(cfg) == lvq.LOOPVQ_ERR_INVALID_ARG, field
+        assert lvq.loopvq_last_error() != ""
+        assert lvq.loopvq_bits_per_elem(cfg) == -1.0
+    assert lvq.loopvq_config_check(good) == 0 and lvq.loopvq_last_error() == ""
+
+
+@pytest.mark.parametrize("wl", W.ALL, ids=[w.name for w in W.ALL])
+def test_layout_query_closed_forms(wl):
+    cfg = lvq.make_config(wl)
+    num_pages = 1000
+    lay = lvq.loopvq_layout_query(cfg, wl.batch, num_pages)
+    ref = O.page_layout(wl.page_tokens, wl.groups, wl.index_bits)
+    assert lay.page_bytes == ref["page_bytes"] and lay.kind_bytes == ref["kind_bytes"]
+    assert lay.tile_bytes == 2 * wl.index_bits
+    assert lay.pool_head_stride_bytes == num_pages * lay.page_bytes
+    assert lay.pool_bytes == wl.layers * wl.loop_groups * wl.kv_heads * num_pages * lay.page_bytes
+    assert lay.codebook_elems == wl.layers * wl.cb_loop_groups * wl.kv_heads * wl.groups * wl.codewords * wl.sub_len
+    assert lay.norms_elems == wl.layers * wl.cb_loop_groups * wl.kv_heads * wl.groups * wl.codewords
+    assert lay.prefix_elems == wl.batch * wl.kv_heads * wl.prefix * wl.head_dim
+    assert lay.recent_elems == wl.batch * wl.kv_heads * wl.recent * wl.head_dim
+    assert lay.bits_per_elem == O.bits_per_elem(wl.index_bits, wl.chans, wl.loop_group)
+    # index bytes of one sequence's VQ rows: n_vq * (d/c) * b/8 per kind, padded to whole pages
+    n_pages = -(-wl.n_vq // wl.page_tokens)
+    assert n_pages * lay.kind_bytes >= wl.n_vq * wl.groups * wl.index_bits // 8
+
+
+def test_layout_query_rejects():
+    cfg = lvq.make_config(W.TINY)
+    with pytest.raises(lvq.LoopVQError) as e:
+        lvq.loopvq_layout_query(cfg, 0, 10)
+    assert e.value.status == lvq.LOOPVQ_ERR_INVALID_ARG
+    with pytest.raises(lvq.LoopVQError):
+        lvq.loopvq_layout_query(cfg, 1, 0)
+
+
+FAKE = 1 << 20   # never dereferenced: every call below fails validation first
+
+
+def _decode_kw(wl, **over):
+    kw = dict(layer=0, loop=0, batch=wl.batch, q=FAKE, seq_lens=FAKE, max_seq_len=wl.context, out=FAKE,
+              block_table=FAKE, pool=FAKE, max_pages_per_seq=600, num_pages=10, cb_k_prep=FAKE, cb_v_prep=FAKE,
+              k_prefix=FAKE, v_prefix=FAKE, k_recent=FAKE, v_recent=FAKE, workspace=None, workspace_bytes=0,
+              stream=0)
+    kw.update(over)
+    return kw
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(layer=24), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(loop=4), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(batch=0), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(q=None), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(pool=None), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(k_recent=None), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(num_splits=300), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(pool=FAKE + 8), lvq.LOOPVQ_ERR_MISALIGNED),
+    (dict(k_prefix=FAKE + 2), lvq.LOOPVQ_ERR_MISALIGNED),
+    (dict(out=FAKE + 2), lvq.LOOPVQ_ERR_MISALIGNED),
+    (dict(num_splits=4), lvq.LOOPVQ_ERR_WORKSPACE),
+])
+def test_decode_rejects_before_launch(over, status):
+    wl = W.STACK_32K
+    cfg = lvq.make_config(wl)
+    with pytest.raises(lvq.LoopVQError) as e:
+        lvq.loopvq_decode_attn(cfg, **_decode_kw(wl, **over))
+    assert e.value.status == status
+
+
+def test_decode_auto_split_workspace_is_checked():
+    wl = W.TINY                                     # 1 query: the plan splits long contexts
+    cfg = lvq.make_config(wl.with_(context=60000))
+    need = lvq.loopvq_decode_attn_workspace(cfg, 1, 60000)
+    assert need > 0
+    with pytest.raises(lvq.LoopVQError) as e:
+        lvq.loopvq_decode_attn(cfg, **_decode_kw(wl, batch=1, max_seq_len=60000, workspace_bytes=need - 1,
+                                                 workspace=FAKE))
+    assert e.value.status == lvq.LOOPVQ_ERR_WORKSPACE
+
+
+def test_unsupported_variants_rejected():
+    for over in [dict(index_bits=9), dict(loop_group=2, num_loops=4), dict(chans_per_group=8, head_dim=256)]:
+        cfg = lvq.make_config(W.LAYER_4K)
+        for k, v in over.items():
+            setattr(cfg, k, v)
+        assert lvq.loopvq_config_check(cfg) == 0
+        with pytest.raises(lvq.LoopVQError) as e:
+            lvq.loopvq_decode_attn(cfg, **_decode_kw(W.LAYER_4K))
+        assert e.value.status == lvq.LOOPVQ_ERR_UNSUPPORTED
+
+
+def _encode_kw(**over):
+    kw = dict(layer=0, loop_group=0, kind=0, n_tokens=10, src=FAKE, stride_loop=4096, stride_token=2048,
+              stride_head=128, seq_id=FAKE, vq_pos=FAKE, block_table=FAKE, batch=2, max_pages_per_seq=4,
+              num_pages=8, cb=FAKE, cb_norms=FAKE, pool=FAKE, stream=0)
+    kw.update(over)
+    return kw
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(kind=2), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(loop_group=1), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(n_tokens=-1), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(cb_norms=None), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(batch=0), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(src=FAKE + 4), lvq.LOOPVQ_ERR_MISALIGNED),
+    (dict(stride_token=2050), lvq.LOOPVQ_ERR_MISALIGNED),
+    (dict(cb=FAKE + 8), lvq.LOOPVQ_ERR_MISALIGNED),
+])
+def test_encode_rejects_before_launch(over, status):
+    cfg = lvq.make_config(W.LAYER_4K)
+    with pytest.raises(lvq.LoopVQError) as e:
+        lvq.loopvq_encode(cfg, **_encode_kw(**over))
+    assert e.value.status == status
+
+
+def test_codebook_prepare_rejects():
+    cfg = lvq.make_config(W.TINY)
+    with pytest.raises(lvq.LoopVQError) as e:
+        lvq.loopvq_codebook_prepare(cfg, None, FAKE, None, stream=0)
+    assert e.value.status == lvq.LOOPVQ_ERR_INVALID_ARG
+    with pytest.raises(lvq.LoopVQError) as e:
+        lvq.loopvq_codebook_prepare(cfg, FAKE + 2, FAKE, None, stream=0)
+    assert e.value.status == lvq.LOOPVQ_ERR_MISALIGNED
+
+
+def test_status_strings():
+    for s, txt in [(0, "ok"), (-1, "invalid argument"), (-2, "unsupported variant"), (-3, "misaligned pointer"),
+                   (-4, "workspace too small"), (-5, "HIP error"), (7, "unknown status")]:
+        assert lvq.loopvq_status_string(s) == txt

@@ -1,0 +1,178 @@
+"""GPU parity of the LoopVQ HIP library against the CPU oracle (needs an MI355X).
+
+Small cases run the whole chain (encode -> packed pages -> decode) and compare
+every index, every page byte and every attention output; full-size cases run
+the workload's decode launch (same shapes and split plan the benchmark times)
+and compare sampled queries.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+H = pytest.importorskip("lvq_harness")
+
+from oracle import loopvq_oracle as O  # noqa: E402
+from synth import workloads as W  # noqa: E402
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _chain(case, decode_splits=(0,), scale=None):
+    """Encode both kinds on the GPU, compare indices and pages, then decode and compare."""
+    wl = case.wl
+    exp = case.oracle_encode()
+    case.gpu_setup()
+    excused = 0
+    for kind in (0, 1):
+        gidx, rows, n_rerank = case.gpu_encode(kind)
+        C_of = case.cbk if kind == 0 else case.cbv
+        for h in range(wl.kv_heads):
+            C = H.codebooks_f64(C_of, case.l, case.jc, h)
+            for b in range(wl.batch):
+                sel = [r for r, (bb, _) in enumerate(rows) if bb == b]
+                if not sel:
+                    continue
+                idx, d1, d2, x = exp[kind, b, h]
+                for g in range(wl.groups):
+                    excused += H.check_indices(gidx[sel, h, g], idx[:, g], d1[:, g], d2[:, g], x[:, g], C[g])
+    # page bytes: the GPU pool equals the oracle's packing of the oracle's indices
+    pool_ref = case.oracle_pool(lambda k, b, h: exp[k, b, h][0])
+    pool_gpu = case.d_pool.cpu().numpy().reshape(pool_ref.shape)
+    if excused == 0:
+        assert np.array_equal(pool_gpu, pool_ref), "packed pages differ"
+    else:
+        assert (pool_gpu != pool_ref).sum() <= excused
+    # decode over the oracle's pages (uploaded), then over the GPU-encoded pages
+    o_ref, lse_ref = case.oracle_decode(lambda k, b, h: exp[k, b, h][0], scale=scale)
+    gpu_pool = case.d_pool.clone()
+    case.d_pool.copy_(torch.from_numpy(pool_ref.reshape(-1)).to(H.DEV))
+    res = []
+    for S in decode_splits:
+        o, lse = case.gpu_decode(num_splits=S, scale=scale or 0.0)
+        res.append(H.check_attention(o, o_ref, lse, lse_ref))
+    case.d_pool.copy_(gpu_pool)
+    if excused == 0:
+        o, lse = case.gpu_decode(num_splits=decode_splits[0], scale=scale or 0.0)
+        H.check_attention(o, o_ref, lse, lse_ref)
+    return excused, res
+
+
+@pytest.mark.parametrize("loop", [0, 1, 2, 3])
+def test_tiny_chain(loop):
+    _say(f"tiny chain loop={loop}")
+    case = H.Case(W.TINY, 0, loop, [W.TINY.context])
+    excused, res = _chain(case, decode_splits=(0, 1, 3))
+    _say(f"  excused={excused} rel/max={res}")
+
+
+SMALL = W.LAYER_4K.with_(batch=6, q_heads=4, kv_heads=4, context=700)
+
+
+@pytest.mark.parametrize("splits", [(0, 1), (3, 7)])
+def test_small_ragged_chain(splits):
+    lens = [700, 1, 72, 73, 137, 391]           # edge cases: one token, no VQ rows, one VQ row, ragged tails
+    _say(f"small ragged chain splits={splits}")
+    case = H.Case(SMALL, 0, 2, lens, seed=1)
+    _chain(case, decode_splits=splits)
+
+
+def test_gqa_chain():
+    wl = SMALL.with_(batch=2, q_heads=8, kv_heads=2, context=600)
+    _say("gqa chain")
+    _chain(H.Case(wl, 0, 1, [600, 333], seed=2), decode_splits=(0, 2))
+
+
+def test_quarter_bit_rotated_chain():
+    wl = W.QUARTER_16K.with_(layers=2, batch=3, q_heads=2, kv_heads=2, context=900)
+    _say("quarter-bit rotated chain")
+    _chain(H.Case(wl, 1, 3, [900, 301, 73], seed=3), decode_splits=(0, 2))
+
+
+def test_per_loop_group_codebooks_chain():
+    wl = SMALL.with_(loops=8, batch=2, q_heads=2, kv_heads=2, context=500, codebook_per_loop_group=True)
+    _say("per-loop-group codebooks chain")
+    _chain(H.Case(wl, 0, 5, [500, 250], seed=4), decode_splits=(0,))
+
+
+def test_d64_page128_chain():
+    wl = W.TINY.with_(batch=3, q_heads=2, kv_heads=2, context=800, page_tokens=128)
+    _say("d64 page128 chain")
+    _chain(H.Case(wl, 0, 3, [800, 200, 450], seed=5), decode_splits=(0, 4))
+
+
+def test_large_scores_take_exact_maximum_path():
+    """Scores far above the first tile's maximum (scale 50x) force the split's exact-maximum redo."""
+    wl = SMALL.with_(batch=2, q_heads=2, kv_heads=2, context=1500)
+    _say("large-score redo path")
+    case = H.Case(wl, 0, 0, [1500, 900], seed=6)
+    _chain(case, decode_splits=(0, 1), scale=50.0 / np.sqrt(wl.head_dim))
+
+
+def test_no_vq_rows_is_plain_attention():
+    wl = SMALL.with_(batch=4, q_heads=2, kv_heads=2, context=72)
+    _say("no VQ rows")
+    case = H.Case(wl, 0, 1, [72, 1, 9, 40], seed=7)
+    case.gpu_setup()
+    exp = {(k, b, h): np.zeros((0, wl.groups), np.int64) for k in (0, 1) for b in range(4) for h in range(2)}
+    o_ref, lse_ref = case.oracle_decode(lambda k, b, h: exp[k, b, h])
+    o, lse = case.gpu_decode()
+    H.check_attention(o, o_ref, lse, lse_ref)
+
+
+def test_decode_is_deterministic_for_one_wave_histograms():
+    """Two runs on the same inputs give outputs within float-summation-order noise (1e-6)."""
+    case = H.Case(SMALL.with_(batch=2, q_heads=2, kv_heads=2), 0, 1, [700, 650], seed=8)
+    exp = case.oracle_encode()
+    case.gpu_setup()
+    pool_ref = case.oracle_pool(lambda k, b, h: exp[k, b, h][0])
+    case.d_pool.copy_(torch.from_numpy(pool_ref.reshape(-1)).to(H.DEV))
+    o1, _ = case.gpu_decode()
+    o2, _ = case.gpu_decode()
+    assert np.abs(o1 - o2).max() <= 1e-6 * max(1.0, np.abs(o1).max())
+
+
+# ---------------------------------------------------------------------------------
+# Full-size launches, sampled queries
+# ---------------------------------------------------------------------------------
+FULL = [
+    (W.LAYER_4K, 0, 3),
+    (W.STACK_32K, 17, 2),
+    (W.QUARTER_16K, 9, 1),
+    (W.DEEP_8K, 2, 29),
+]
+
+
+@pytest.mark.parametrize("wl,layer,loop", FULL, ids=[w.name for w, _, _ in FULL])
+def test_full_size_decode_sampled(wl, layer, loop):
+    rng = np.random.default_rng(wl.wid)
+    samples = [(int(rng.integers(wl.batch)), int(rng.integers(wl.q_heads))) for _ in range(6)]
+    samples += [(0, 0), (wl.batch - 1, wl.q_heads - 1)]
+    _say(f"full-size {wl.name} layer={layer} loop={loop} samples={samples}")
+    fc = H.FullCase(wl, layer, loop, samples)
+    fc.upload()
+    o, lse = fc.gpu_decode()
+    for b, hq in samples:
+        o_ref, lse_ref = fc.oracle(b, hq)
+        H.check_attention(o[b, hq][None], o_ref[None], np.array([lse[b, hq]]), np.array([lse_ref]))
+    _say("  ok")
+
+
+def test_full_size_ragged_decode_sampled():
+    wl = W.LAYER_4K
+    lens = np.random.default_rng(11).integers(1, wl.context + 1, wl.batch)
+    lens[:4] = [wl.context, 1, 72, 73]
+    samples = [(b, hq) for b in range(8) for hq in (0, 15)]
+    _say("full-size ragged layer decode")
+    fc = H.FullCase(wl, 0, 1, samples, lens=lens)
+    fc.upload()
+    o, lse = fc.gpu_decode()
+    for b, hq in samples:
+        o_ref, lse_ref = fc.oracle(b, hq)
+        H.check_attention(o[b, hq][None], o_ref[None], np.array([lse[b, hq]]), np.array([lse_ref]))
