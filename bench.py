@@ -1,0 +1,306 @@
+"""Benchmark: LoopVQ decode-attention throughput on one MI355X.
+
+One step = one decode step of a looped transformer stack over a packed,
+loop-axis vector-quantized KV cache: for every loop step t (outer) and layer l
+(inner), one decode-attention launch over all B sequences x Hq heads; then, per
+(layer, loop group, K/V), the encode of the B tokens that leave the bf16 recent
+window (written to a fixed VQ position so the cache stays the same size).
+
+Default workload: 24 layers x 4 loop steps, 16 heads, head_dim 128, batch 64,
+32768-token context, 0.5 bit/elem (c=4, G=4, 8-bit indices), 8 prefix + 64 recent
+bf16 tokens.  The cache is built on the GPU (device generator -> GPU encode).
+
+Prints one JSON line.  `value` is decode queries per second (one query = one
+(layer, loop step, sequence, q-head) attention row over the whole context).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "VQ decode-attn queries/s + effective HBM GB/s (% peak), 32K ctx, 0.5 bit/elem"
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stack32k_traffic.md")
+DECODE_SRC = os.path.join(ROOT, "sub_bit_loop_loopvq_amd", "csrc", "decode_attn.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(wl) -> dict:
+    """Bytes one decode launch must move: index streams, bf16 windows, codebook slices, q in / out."""
+    B, H, Hq, d, c = wl.batch, wl.kv_heads, wl.q_heads, wl.head_dim, wl.chans
+    idx = B * H * wl.n_vq * (d // c) * (wl.index_bits / 8) * 2
+    window = B * H * min(wl.context, wl.prefix + wl.recent) * d * 2 * 2
+    slices = H * (d // c) * wl.codewords * c * 2 * 2
+    qo = B * Hq * d * (2 + 4)
+    rot = d * d * 4 if wl.rotate_keys else 0
+    return {"idx": idx, "window": window, "slices": slices, "q_out": qo, "rot": rot,
+            "total": idx + window + slices + qo + rot}
+
+
+def traffic_from_profile():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it was taken
+    on the current decode kernel source (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_sha and m_val):
+        return None
+    sha = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    return float(m_val.group(1)) if sha == m_sha.group(1) else None
+
+
+class Bench:
+    def __init__(self, wl, seed=0):
+        import torch
+        import sub_bit_loop_loopvq_amd as lvq
+        from synth import gen
+        from synth.device import DeviceGen
+        self.torch, self.lvq, self.wl = torch, lvq, wl
+        dev = "cuda"
+        L, T, G, J = wl.layers, wl.loops, wl.loop_group, wl.loop_groups
+        B, H, Hq, d, P, R = wl.batch, wl.kv_heads, wl.q_heads, wl.head_dim, wl.prefix, wl.recent
+        self.cfg = lvq.make_config(wl)
+        n_vq = wl.n_vq
+        self.pages_per_seq = -(-n_vq // wl.page_tokens)
+        self.num_pages = B * self.pages_per_seq
+        self.lay = lvq.loopvq_layout_query(self.cfg, B, self.num_pages)
+        perm = np.random.default_rng(seed).permutation(self.num_pages).astype(np.int32)
+        self.bt = torch.from_numpy(perm.reshape(B, self.pages_per_seq)).to(dev)
+        self.lens = torch.full((B,), wl.context, dtype=torch.int32, device=dev)
+        t0 = time.time()
+        sc = gen.scales(wl)
+        self.prep, self.cb, self.norms = {}, {}, {}
+        for kind in (0, 1):
+            cbh = gen.codebooks(wl, kind, sc)
+            self.cb[kind] = torch.from_numpy(cbh.view(np.int16)).to(dev)
+            self.prep[kind] = torch.empty_like(self.cb[kind])
+            self.norms[kind] = torch.empty(self.lay.norms_elems, dtype=torch.float32, device=dev)
+            lvq.loopvq_codebook_prepare(self.cfg, self.cb[kind], self.prep[kind], self.norms[kind])
+        log(f"codebooks ready ({time.time() - t0:.1f}s)")
+        q = np.stack([np.stack([gen.queries(wl, l, t) for t in range(T)]) for l in range(L)])
+        self.q = torch.from_numpy(q.view(np.int16)).to(dev)                  # [L][T][B][Hq][d]
+        self.rot = (torch.from_numpy(gen.rotation_matrix_f32(wl)).to(dev) if wl.rotate_keys else None)
+        log(f"queries ready ({time.time() - t0:.1f}s)")
+        dg = DeviceGen(wl)
+        # bf16 windows of every (layer, loop step): [2][L][T][B][Hkv][P or R][d]
+        self.pre = torch.empty((2, L, T, B, H, P, d), dtype=torch.int16, device=dev)
+        self.rec = torch.empty((2, L, T, B, H, R, d), dtype=torch.int16, device=dev)
+        for kind in (0, 1):
+            for l in range(L):
+                dg.kv(self.pre[kind, l], kind=kind, layer=l, b0=0, nb=B, h0=0, nh=H, n0=0, nn=P, t0=0, nt=T,
+                      s_loop=B * H * P * d, s_b=H * P * d, s_h=P * d, s_n=d)
+                dg.kv(self.rec[kind, l], kind=kind, layer=l, b0=0, nb=B, h0=0, nh=H, n0=wl.context - R, nn=R,
+                      t0=0, nt=T, s_loop=B * H * R * d, s_b=H * R * d, s_h=R * d, s_n=d)
+        torch.cuda.synchronize()
+        log(f"windows ready ({time.time() - t0:.1f}s)")
+        # packed index pool: device-generated K/V of every VQ token, encoded on the GPU
+        self.pool = torch.zeros(self.lay.pool_bytes, dtype=torch.uint8, device=dev)
+        chunk = max(1, min(B, int(2.5e9 // (G * n_vq * H * d * 2))))
+        src = torch.empty((G, chunk * n_vq, H, d), dtype=torch.int16, device=dev)
+        rows = chunk * n_vq
+        self.rerank = torch.zeros(1, dtype=torch.int64, device=dev)
+        for l in range(L):
+            for j in range(J):
+                for kind in (0, 1):
+                    for b0 in range(0, B, chunk):
+                        nb = min(chunk, B - b0)
+                        for bi in range(nb):
+                            dg.kv(src[:, bi * n_vq:], kind=kind, layer=l, b0=b0 + bi, nb=1, h0=0, nh=H, n0=P,
+                                  nn=n_vq, t0=j * G, nt=G, s_loop=rows * H * d, s_b=0, s_h=d, s_n=H * d)
+                        r = torch.arange(nb * n_vq, dtype=torch.int32, device=dev)
+                        lvq.loopvq_encode(self.cfg, layer=l, loop_group=j, kind=kind, n_tokens=nb * n_vq, src=src,
+                                          stride_loop=rows * H * d, stride_token=H * d, stride_head=d,
+                                          seq_id=r // n_vq + b0, vq_pos=r % n_vq, block_table=self.bt, batch=B,
+                                          max_pages_per_seq=self.pages_per_seq, num_pages=self.num_pages,
+                                          cb=self.cb[kind], cb_norms=self.norms[kind], pool=self.pool,
+                                          rerank_count=self.rerank)
+            torch.cuda.synchronize()
+            log(f"layer {l} encoded ({time.time() - t0:.1f}s)")
+        del src
+        torch.cuda.empty_cache()
+        self.ws_bytes = lvq.loopvq_decode_attn_workspace(self.cfg, B, wl.context)
+        self.ws = torch.empty(max(16, self.ws_bytes), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        self.evict_seq = torch.arange(B, dtype=torch.int32, device=dev)
+        self.evict_pos = torch.full((B,), n_vq - 1, dtype=torch.int32, device=dev)
+        self.setup_s = time.time() - t0
+        log(f"setup done in {self.setup_s:.1f}s; re-ranked sub-vectors during build: {int(self.rerank.item())}")
+
+    def decode(self, l, t):
+        wl = self.wl
+        self.lvq.loopvq_decode_attn(
+            self.cfg, layer=l, loop=t, batch=wl.batch, q=self.q[l, t], seq_lens=self.lens, max_seq_len=wl.context,
+            out=self.out, block_table=self.bt, pool=self.pool, max_pages_per_seq=self.pages_per_seq,
+            num_pages=self.num_pages, cb_k_prep=self.prep[0], cb_v_prep=self.prep[1], k_prefix=self.pre[0, l, t],
+            v_prefix=self.pre[1, l, t], k_recent=self.rec[0, l, t], v_recent=self.rec[1, l, t], rot=self.rot,
+            workspace=self.ws, workspace_bytes=self.ws_bytes)
+
+    def evict(self, l, j, kind, slot=0):
+        """Encode the token leaving the recent window of every sequence (ring slot `slot`)."""
+        wl = self.wl
+        B, H, R, d, T = wl.batch, wl.kv_heads, wl.recent, wl.head_dim, wl.loops
+        src = self.rec[kind, l, j * wl.loop_group]
+        self.lvq.loopvq_encode(self.cfg, layer=l, loop_group=j, kind=kind, n_tokens=B,
+                               src=src.data_ptr() + slot * d * 2, stride_loop=B * H * R * d, stride_token=H * R * d,
+                               stride_head=R * d, seq_id=self.evict_seq, vq_pos=self.evict_pos, block_table=self.bt,
+                               batch=B, max_pages_per_seq=self.pages_per_seq, num_pages=self.num_pages,
+                               cb=self.cb[kind], cb_norms=self.norms[kind], pool=self.pool)
+
+    def step(self, events=None):
+        wl = self.wl
+        E = self.torch.cuda.Event
+        for t in range(wl.loops):
+            for l in range(wl.layers):
+                if events is not None:
+                    e0, e1 = E(enable_timing=True), E(enable_timing=True)
+                    e0.record()
+                    self.decode(l, t)
+                    e1.record()
+                    events.append((e0, e1))
+                else:
+                    self.decode(l, t)
+        for l in range(wl.layers):
+            for j in range(wl.loop_groups):
+                for kind in (0, 1):
+                    self.evict(l, j, kind)
+
+
+def cpu_baseline(wl, seconds: float) -> dict:
+    """The CPU oracle (fp64, single BLAS thread) on sampled decode queries of the same workload."""
+    from threadpoolctl import threadpool_limits
+    from oracle import loopvq_oracle as O
+    from synth import gen
+    t_start = time.time()
+    sc = gen.scales(wl)
+    l, t = 0, 0
+    j, tau = t // wl.loop_group, t % wl.loop_group
+    cbk = gen.bf16_to_f64(gen.codebooks(wl, 0, sc, layers=[l])[l, 0])
+    cbv = gen.bf16_to_f64(gen.codebooks(wl, 1, sc, layers=[l])[l, 0])
+    q = gen.queries(wl, l, t)
+    n_pre, n_vq, n_rec = O.split_context(wl.context, wl.prefix, wl.recent)
+    grp = wl.q_heads // wl.kv_heads
+    done, busy = 0, 0.0
+    with threadpool_limits(limits=1):
+        for qi in range(wl.batch * wl.q_heads):
+            b, hq = divmod(qi, wl.q_heads)
+            h = hq // grp
+            win = {}
+            for kind in (0, 1):
+                pre = gen.bf16_to_f64(gen.kv_tokens(wl, kind, l, b, h, 0, n_pre, t, t + 1, sc)[:, 0])
+                rec = gen.bf16_to_f64(gen.kv_tokens(wl, kind, l, b, h, wl.context - n_rec, wl.context, t, t + 1,
+                                                    sc)[:, 0])
+                win[kind] = (pre, rec)
+            ik = gen.random_indices(wl, 0, l, j, b, h, n_vq)
+            iv = gen.random_indices(wl, 1, l, j, b, h, n_vq)
+            pages = O.pack_sequence(ik, iv, wl.page_tokens, wl.index_bits)
+            c0 = time.perf_counter()
+            ik2, iv2 = O.unpack_sequence(pages, n_vq, wl.groups, wl.page_tokens, wl.index_bits)
+            O.decode_query(gen.bf16_to_f64(q[b, hq]), win[0][0], win[1][0], ik2, iv2, cbk[h], cbv[h], win[0][1],
+                           win[1][1], tau, wl.chans, 1.0 / np.sqrt(wl.head_dim))
+            busy += time.perf_counter() - c0
+            done += 1
+            if busy >= seconds:
+                break
+    return {"value": done / busy, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{done} decode queries (layer 0, loop step 0, sequences 0..{(done - 1) // wl.q_heads}) at "
+                       f"full context {wl.context}: unpack packed pages + dequantize + fp64 softmax attention; "
+                       f"{busy:.1f}s of timed oracle work, 1 BLAS thread; input setup untimed "
+                       f"(wall {time.time() - t_start:.1f}s)")}
+
+
+def copy_calibration(nbytes: int, reps: int) -> None:
+    """A plain device copy of known size, for scaling HBM counters (rocprofv3 --pmc)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="stack24x4_h16_d128_b64_n32k")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, help="bytes; run only a plain copy (counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 5)
+        return
+    import torch
+    from synth import workloads as W
+    wl = W.BY_NAME[args.workload]
+    torch.cuda.set_device(0)
+    bench = Bench(wl)
+    for _ in range(args.warmup):
+        bench.step()
+    torch.cuda.synchronize()
+    events = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        bench.step(events)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = ev0.elapsed_time(ev1) / args.steps
+    launch_us = np.array([a.elapsed_time(b) * 1e3 for a, b in events])
+    ab = algorithmic_bytes(wl)
+    q_per_step = wl.layers * wl.loops * wl.queries_per_launch
+    value = q_per_step / (step_ms * 1e-3)
+    avg_us = float(launch_us.mean())
+    achieved = ab["total"] / (avg_us * 1e-6) / 1e9
+    traffic = traffic_from_profile()
+    log(f"wall {wall:.2f}s for {args.steps} steps; launch avg {avg_us:.1f} us (p10 {np.percentile(launch_us, 10):.1f}, "
+        f"p90 {np.percentile(launch_us, 90):.1f}); {achieved:.0f} GB/s")
+    rec = {
+        "metric": METRIC, "value": value, "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "layers": wl.layers, "loop_steps": wl.loops, "loop_group": wl.loop_group,
+                   "q_heads": wl.q_heads, "kv_heads": wl.kv_heads, "head_dim": wl.head_dim, "batch": wl.batch,
+                   "context": wl.context, "prefix_tokens": wl.prefix, "recent_tokens": wl.recent,
+                   "chans_per_group": wl.chans, "index_bits": wl.index_bits,
+                   "bits_per_elem": wl.index_bits / (wl.chans * wl.loop_group), "page_tokens": wl.page_tokens,
+                   "launches_per_step": wl.layers * wl.loops,
+                   "eviction_encodes_per_step": wl.layers * wl.loop_groups * 2},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
+        "decode_launch_us": {"mean": avg_us, "p10": float(np.percentile(launch_us, 10)),
+                             "p50": float(np.percentile(launch_us, 50)), "p90": float(np.percentile(launch_us, 90))},
+        "algorithmic_bytes_per_launch": ab,
+        "step_gbps": ab["total"] * wl.layers * wl.loops / (step_ms * 1e-3) / 1e9,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -95,14 +95,23 @@ Sizes sizes_of(const loopvq_config* c) {
 // Tokens per wave tile of the decode kernel (1 KB of 8-bit indices).
 int decode_tile_tokens(const loopvq_config* c) { return 256 / ((c->head_dim / c->chans_per_group) / 4); }
 
+// Fewest splits the decode kernel accepts: one split covers at most 2040 tiles (a wave
+// walks at most 255 of them, and the 64-bit value histogram cannot overflow).
+int min_splits(const loopvq_config* c, int32_t max_seq_len) {
+  const int64_t n_vq = std::max<int64_t>(0, int64_t(max_seq_len) - c->prefix_tokens - c->recent_tokens);
+  const int64_t tiles = (n_vq + decode_tile_tokens(c) - 1) / decode_tile_tokens(c);
+  return (int)std::max<int64_t>(1, (tiles + 2039) / 2040);
+}
+
 int plan_splits(const loopvq_config* c, int32_t batch, int32_t max_seq_len) {
   const int64_t Q = int64_t(batch) * c->num_q_heads;
   const int64_t n_vq = std::max<int64_t>(0, int64_t(max_seq_len) - c->prefix_tokens - c->recent_tokens);
   const int64_t tiles = (n_vq + decode_tile_tokens(c) - 1) / decode_tile_tokens(c);
-  const int64_t slots = 512;  // 256 CUs x 2 resident workgroups
+  const int64_t slots = 256;  // one resident decode workgroup per CU
   int64_t S = Q >= slots ? 1 : (slots + Q - 1) / Q;
-  const int64_t max_by_work = std::max<int64_t>(1, tiles / 16);   // >= 16 tiles per split
+  const int64_t max_by_work = std::max<int64_t>(1, tiles / 32);   // >= 32 tiles per split
   S = std::min(S, max_by_work);
+  S = std::max<int64_t>(S, min_splits(c, max_seq_len));
   return (int)std::max<int64_t>(1, std::min<int64_t>(S, 256));
 }
 
@@ -264,6 +273,9 @@ loopvq_status loopvq_decode_attn(const loopvq_config* cfg, const loopvq_decode_a
       !aligned(a->seq_lens, 4))
     return fail(LOOPVQ_ERR_MISALIGNED, "q, out, lse, rot or seq_lens misaligned");
   const int S = a->num_splits > 0 ? a->num_splits : plan_splits(cfg, a->batch, a->max_seq_len);
+  if (S < min_splits(cfg, a->max_seq_len) || S > 256)
+    return fail(LOOPVQ_ERR_INVALID_ARG, "num_splits %d: a context of %d tokens needs between %d and 256 splits", S,
+                a->max_seq_len, min_splits(cfg, a->max_seq_len));
   const int64_t Q = int64_t(a->batch) * cfg->num_q_heads;
   const size_t need = S > 1 ? size_t(S) * Q * (cfg->head_dim + 4) * sizeof(float) : 0;
   if (workspace_bytes < need || (need && !workspace))

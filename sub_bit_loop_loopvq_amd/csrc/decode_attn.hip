@@ -9,27 +9,33 @@
 // loop-step-(t mod G) slice of that codeword.
 //
 // How (MI355X):
-//  * one workgroup = one query x one token split; 4 waves.
-//  * prologue: q' = scale*log2(e) * R^T q; then the q.codeword lookup table
+//  * one workgroup = one query x one token split; 8 waves; one workgroup per CU
+//    (128 KB of LDS).
+//  * prologue: q' = scale*log2(e) * R^T q; the q.codeword lookup table
 //    LUT[k][g] = q'_g . slice_tau(C_k[g]) is built in LDS (K x NG fp32).
-//  * LDS row per codeword k (256 B): LUT entries at byte 4*g (NG=32) or two
-//    copies at 4*g and 64 + 4*g (NG=16, so 64 lanes cover all 32 banks), and
-//    the value histogram at byte 128 + the same offsets.  The LDS address of
-//    (k, g) is k*256 + byte(g): one v_perm_b32 places the packed index byte
-//    next to the lane's group byte, so an index costs one VALU op + one LDS op.
+//  * LDS layout, [0, 64K): one 256-byte row per codeword k holding LUT[k][g] at
+//    byte 4*g (NG=32) or two copies at 4*g and 64 + 4*g (NG=16, so the 64 lanes
+//    of a read cover all 32 banks).  [64K, 128K): the value histogram, one
+//    256-byte row per codeword, H[k][g] as a 64-bit integer at byte 8*g.  The
+//    address of either entry is (region byte, index byte, group byte): one
+//    v_perm_b32 merges the packed index byte with two constant bytes, so an
+//    index costs one VALU op plus one LDS op.
 //  * index stream: a wave reads one 1 KB block of K indices and one of V
-//    indices per tile (32 tokens at NG=32, 64 at NG=16), 16 B per lane.  Lane
-//    (Q, u) holds 4 tokens x 4 groups; its 16 lookups walk the groups in an
-//    order rotated by Q so the lanes of one instruction hit distinct banks.
+//    indices per tile (32 tokens at NG=32, 64 at NG=16), 16 B per lane, four
+//    tiles in flight.  Lane (Q, u) holds 4 tokens x 4 groups; its 16 lookups walk
+//    the groups in an order rotated by Q so the lanes of one instruction hit
+//    distinct banks.  Page ids of the wave's tiles are vector-loaded once and
+//    read back with v_readlane.
 //  * token scores: per-lane partial sums + a 2-3 step DPP reduce-scatter over
 //    the lanes of a token quad, so each lane ends with one full token score.
-//  * softmax: scores live in log2 units; p = exp2(s - m_ref) with m_ref the
-//    maximum over the first tile of every wave, capped at 2^64.  A split where
-//    any later score exceeds m_ref by more than 64 is recomputed with the exact
-//    maximum (rare; keeps fp32 sums finite with no per-tile rescaling of the
-//    histogram).
-//  * values: H[idx_V[n][g]][g] += p_n with LDS float atomics; after the token
-//    loop, o[g*c + i] = sum_k H[k][g] * Cv_tau[k][g*c + i] (K*d MACs per split).
+//  * softmax: scores in log2 units; p = exp2(s - m_ref), m_ref = maximum over
+//    the first tile of every wave.  A split where a later score exceeds m_ref by
+//    more than 17 (log2 units) is recomputed with the exact maximum (rare).
+//  * values: H[idx_V[n][g]][g] += floor(p_n * 2^30) with 64-bit LDS integer
+//    atomics (exact and order independent, so the output is bitwise
+//    reproducible; LDS float atomics are an order of magnitude slower on this
+//    part).  Afterwards o[g*c + i] = sum_k H[k][g] * Cv_tau[k][g*c + i] and the
+//    normaliser is sum_k H[k][0]: the same quantised weights.
 //  * bf16 windows: lane-per-token scores, then lane-per-channel value sums.
 //  * splits write (m, l, o) partials; a second kernel merges them with
 //    log-sum-exp.  One split writes the output directly.
@@ -41,29 +47,40 @@ namespace lvq {
 namespace {
 
 constexpr int kRowBytes = 256;
-constexpr int kHOff = 128;
-constexpr float kThr = 64.f;
+constexpr float kThr = 17.f;            // p <= 2^17 before a redo is forced
+constexpr float kFix = 1073741824.f;    // 2^30: fixed-point scale of the histogram
 constexpr float kNegInf = -INFINITY;
+constexpr int kWaves = 8;
+constexpr int kMaxTilesPerWave = 256;   // page-id vector: 4 VGPRs of 64 lanes
 
 template <int D, int WAVES>
 struct DecodeSmem {
-  uint8_t tab[kCodes * kRowBytes];       // LUT + histogram rows (must stay first: LDS offset 0)
-  float q[D];                            // q' (log2 units)
-  float red[WAVES * 64 > D ? WAVES * 64 : D];  // raw q, then contraction partials
-  float wo[WAVES][D];                    // window partial o per wave
-  float wm[WAVES], wl[WAVES];            // window partial max / sum per wave
-  float vm[WAVES], vl[WAVES];            // VQ max / sum per wave
+  uint8_t lut[kCodes * kRowBytes];              // [0, 64K): LUT rows (must stay first)
+  unsigned long long hist[kCodes * 32];         // [64K, 128K): u64 histogram rows
+  float q[D];                                   // q' (log2 units)
+  float red[WAVES * 64 > D ? WAVES * 64 : D];   // raw q, then contraction partials
+  float wo[WAVES][D];                           // window partial o per wave
+  float wm[WAVES], wl[WAVES];                   // window partial max / sum per wave
+  float vm[WAVES];                              // VQ max per wave
   int vover[WAVES];
 };
 
 __device__ __forceinline__ u32x4 ntload(const u32x4* ptr) { return __builtin_nontemporal_load(ptr); }
 
-__device__ __forceinline__ float lds_f32(const uint8_t* tab, uint32_t addr) {
-  return *reinterpret_cast<const float*>(tab + addr);
+__device__ __forceinline__ float lds_f32(const uint8_t* lds, uint32_t addr) {
+  return *reinterpret_cast<const float*>(lds + addr);
+}
+
+// p in [0, 2^17] -> floor(p * 2^30) as (hi, lo) 32-bit halves, exactly
+__device__ __forceinline__ void to_fixed(float p, uint32_t& hi, uint32_t& lo) {
+  const float hf = floorf(p * 0.25f);                        // = floor(p * 2^30 / 2^32)
+  const float lf = fmaf(hf, -4294967296.f, p * kFix);        // exact remainder in [0, 2^32)
+  hi = (uint32_t)hf;
+  lo = (uint32_t)lf;
 }
 
 template <int NG, int C, int WAVES>
-__global__ void __launch_bounds__(WAVES * 64, 2) decode_kernel(DecodeParams p) {
+__global__ void __launch_bounds__(WAVES * 64, 1) decode_kernel(DecodeParams p) {
   constexpr int D = NG * C;
   constexpr int G4 = NG / 4;        // lanes that share a token quad
   constexpr int TW = 256 / G4;      // tokens per wave tile (1 KB of 8-bit indices)
@@ -73,6 +90,7 @@ __global__ void __launch_bounds__(WAVES * 64, 2) decode_kernel(DecodeParams p) {
   static_assert(CPL == 1 || CPL == 2 || CPL == 4, "D");
 
   __shared__ DecodeSmem<D, WAVES> sm;
+  uint8_t* const lds = sm.lut;      // LDS address 0 (histogram at 65536)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -146,12 +164,12 @@ __global__ void __launch_bounds__(WAVES * 64, 2) decode_kernel(DecodeParams p) {
         acc = fmaf(qg[6], bf16_lo(w.w), acc);
         acc = fmaf(qg[7], bf16_hi(w.w), acc);
       }
-      float* row = reinterpret_cast<float*>(sm.tab + k * kRowBytes);
+      float* row = reinterpret_cast<float*>(lds + k * kRowBytes);
       row[g] = acc;
       if constexpr (NG == 16) row[16 + g] = acc;
     }
-    for (int e = tid; e < kCodes * 32; e += NT)
-      reinterpret_cast<float*>(sm.tab + (e >> 5) * kRowBytes + kHOff)[e & 31] = 0.f;
+    u32x4* hz = reinterpret_cast<u32x4*>(sm.hist);
+    for (int e = tid; e < kCodes * 32 * 8 / 16; e += NT) hz[e] = u32x4{0u, 0u, 0u, 0u};
   }
 
   // ---- 3. bf16 window rows (prefix + recent) of this split ------------------------------
@@ -225,38 +243,58 @@ __global__ void __launch_bounds__(WAVES * 64, 2) decode_kernel(DecodeParams p) {
   __syncthreads();   // LUT, histogram zeroing and window partials complete
 
   // ---- 4. vector-quantized rows ---------------------------------------------------------
-  float m_ref = kNegInf, l_vq = 0.f;
+  float m_ref = kNegInf;
   if (has_vq) {
     const int Qd = lane / G4, u = lane % G4;
-    uint32_t base[4], sel[4];
+    uint32_t base_l[4], sel_l[4], base_h[4], sel_h[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint32_t gg = 4u * u + ((r + Qd) & 3);
-      base[r] = gg * 4u + ((NG == 16) ? (uint32_t)(Qd & 1) * 64u : 0u);
-      sel[r] = 0x0c0c0000u | ((4u + ((r + Qd) & 3)) << 8);
+      const uint32_t rr = (r + Qd) & 3;
+      const uint32_t gg = 4u * u + rr;
+      base_l[r] = gg * 4u + ((NG == 16) ? (uint32_t)(Qd & 1) * 64u : 0u);
+      sel_l[r] = 0x0c0c0000u | ((4u + rr) << 8);             // [0, 0, idx, base.b0]
+      base_h[r] = 0x00010000u | (gg * 8u);
+      sel_h[r] = 0x0c020000u | ((4u + rr) << 8);             // [0, base.b2 = 1, idx, base.b0]
     }
     const int tok = (NG == 16) ? u : (((u >= 4) ? 2 : 0) + ((u & 2) ? 1 : 0));
-    const bool hi = (u >= 4);
-    const uint8_t* pool_h = p.pool_lj + (int64_t)h * p.head_stride;
+    const bool hi_half = (u >= 4);
+    const uint8_t* pool_h = p.pool_lj + (int64_t)h * p.head_stride + lane * 16;
     const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
     const int pt_mask = (1 << p.pt_shift) - 1;
 
-    auto tile_ptr = [&](int t) -> const uint8_t* {
-      const int u0 = t * TW;
-      int pg = bt[u0 >> p.pt_shift];
-      if (pg < 0 || pg >= p.num_pages) pg = 0;
-      return pool_h + (int64_t)pg * p.page_bytes + (int64_t)(u0 & pt_mask) * NG + lane * 16;
+    const int my_first = t0 + wave;
+    const int n_my = (my_first < t1) ? (t1 - my_first + WAVES - 1) / WAVES : 0;
+
+    // page ids of this wave's tiles: lane l of pg[c] holds the page of tile 64*c + l
+    int pg[kMaxTilesPerWave / 64];
+#pragma unroll
+    for (int c = 0; c < kMaxTilesPerWave / 64; ++c) {
+      const int i = 64 * c + lane;
+      int v = 0;
+      if (i < n_my) {
+        v = bt[((my_first + i * WAVES) * TW) >> p.pt_shift];
+        v = (v < 0 || v >= p.num_pages) ? 0 : v;
+      }
+      pg[c] = v;
+    }
+    auto tile_ptr = [&](int i) -> const uint8_t* {   // i: wave-uniform tile ordinal
+      const int c = i >> 6, l = i & 63;
+      const int p0 = __builtin_amdgcn_readlane(pg[0], l), p1 = __builtin_amdgcn_readlane(pg[1], l);
+      const int p2 = __builtin_amdgcn_readlane(pg[2], l), p3 = __builtin_amdgcn_readlane(pg[3], l);
+      const int page = c == 0 ? p0 : (c == 1 ? p1 : (c == 2 ? p2 : p3));
+      const int u0 = (my_first + i * WAVES) * TW;
+      return pool_h + (int64_t)page * p.page_bytes + (int64_t)(u0 & pt_mask) * NG;
     };
 
-    auto score = [&](const u32x4 xk, int t) -> float {
+    auto score = [&](const u32x4 xk, bool masked, int i) -> float {
       const uint32_t xs[4] = {xk.x, xk.y, xk.z, xk.w};
       float acc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float a = lds_f32(sm.tab, __builtin_amdgcn_perm(xs[i], base[0], sel[0]));
+      for (int j = 0; j < 4; ++j) {
+        float a = lds_f32(lds, __builtin_amdgcn_perm(xs[j], base_l[0], sel_l[0]));
 #pragma unroll
-        for (int r = 1; r < 4; ++r) a += lds_f32(sm.tab, __builtin_amdgcn_perm(xs[i], base[r], sel[r]));
-        acc[i] = a;
+        for (int r = 1; r < 4; ++r) a += lds_f32(lds, __builtin_amdgcn_perm(xs[j], base_l[r], sel_l[r]));
+        acc[j] = a;
       }
       float sc;
       if constexpr (NG == 16) {
@@ -268,8 +306,8 @@ __global__ void __launch_bounds__(WAVES * 64, 2) decode_kernel(DecodeParams p) {
         const float kk = b1 ? c1 : c0, ss = b1 ? c0 : c1;
         sc = kk + dpp<dpp_quad(1, 0, 3, 2)>(ss);
       } else {
-        const float k0 = hi ? acc[2] : acc[0], s0 = hi ? acc[0] : acc[2];
-        const float k1 = hi ? acc[3] : acc[1], s1 = hi ? acc[1] : acc[3];
+        const float k0 = hi_half ? acc[2] : acc[0], s0 = hi_half ? acc[0] : acc[2];
+        const float k1 = hi_half ? acc[3] : acc[1], s1 = hi_half ? acc[1] : acc[3];
         const float c0 = k0 + dpp<kDppRowHalfMirror>(s0);
         const float c1 = k1 + dpp<kDppRowHalfMirror>(s1);
         const bool b2 = (u & 2) != 0;
@@ -277,46 +315,62 @@ __global__ void __launch_bounds__(WAVES * 64, 2) decode_kernel(DecodeParams p) {
         const float d0 = kk + dpp<dpp_quad(2, 3, 0, 1)>(ss);
         sc = d0 + dpp<dpp_quad(1, 0, 3, 2)>(d0);
       }
-      const bool valid = t * TW + 4 * Qd + tok < n_vq;
-      return valid ? sc : kNegInf;
+      if (masked) {
+        const int pos = (my_first + i * WAVES) * TW + 4 * Qd + tok;
+        sc = pos < n_vq ? sc : kNegInf;
+      }
+      return sc;
     };
 
     auto accum_v = [&](const u32x4 xv, float pp) {
-      float pi[4];
+      uint32_t fh, fl;
+      to_fixed(pp, fh, fl);
+      uint32_t ph[4], pl[4];
       if constexpr (NG == 16) {
-        pi[0] = dpp<dpp_quad(0, 0, 0, 0)>(pp);
-        pi[1] = dpp<dpp_quad(1, 1, 1, 1)>(pp);
-        pi[2] = dpp<dpp_quad(2, 2, 2, 2)>(pp);
-        pi[3] = dpp<dpp_quad(3, 3, 3, 3)>(pp);
+        ph[0] = __builtin_amdgcn_update_dpp(0, fh, dpp_quad(0, 0, 0, 0), 0xf, 0xf, false);
+        ph[1] = __builtin_amdgcn_update_dpp(0, fh, dpp_quad(1, 1, 1, 1), 0xf, 0xf, false);
+        ph[2] = __builtin_amdgcn_update_dpp(0, fh, dpp_quad(2, 2, 2, 2), 0xf, 0xf, false);
+        ph[3] = __builtin_amdgcn_update_dpp(0, fh, dpp_quad(3, 3, 3, 3), 0xf, 0xf, false);
+        pl[0] = __builtin_amdgcn_update_dpp(0, fl, dpp_quad(0, 0, 0, 0), 0xf, 0xf, false);
+        pl[1] = __builtin_amdgcn_update_dpp(0, fl, dpp_quad(1, 1, 1, 1), 0xf, 0xf, false);
+        pl[2] = __builtin_amdgcn_update_dpp(0, fl, dpp_quad(2, 2, 2, 2), 0xf, 0xf, false);
+        pl[3] = __builtin_amdgcn_update_dpp(0, fl, dpp_quad(3, 3, 3, 3), 0xf, 0xf, false);
       } else {
-        const float a = dpp<dpp_quad(0, 0, 0, 0)>(pp);
-        const float bb = dpp<dpp_quad(2, 2, 2, 2)>(pp);
-        const float am = dpp<kDppRowHalfMirror>(a);
-        const float bm = dpp<kDppRowHalfMirror>(bb);
-        pi[0] = hi ? am : a;
-        pi[1] = hi ? bm : bb;
-        pi[2] = hi ? a : am;
-        pi[3] = hi ? bb : bm;
+        // token i of the quad lives in lanes 2i, 2i+1 of the 8-lane group
+        const uint32_t ah = __builtin_amdgcn_update_dpp(0, fh, dpp_quad(0, 0, 0, 0), 0xf, 0xf, false);
+        const uint32_t bh = __builtin_amdgcn_update_dpp(0, fh, dpp_quad(2, 2, 2, 2), 0xf, 0xf, false);
+        const uint32_t al = __builtin_amdgcn_update_dpp(0, fl, dpp_quad(0, 0, 0, 0), 0xf, 0xf, false);
+        const uint32_t bl = __builtin_amdgcn_update_dpp(0, fl, dpp_quad(2, 2, 2, 2), 0xf, 0xf, false);
+        const uint32_t amh = __builtin_amdgcn_update_dpp(0, ah, kDppRowHalfMirror, 0xf, 0xf, false);
+        const uint32_t bmh = __builtin_amdgcn_update_dpp(0, bh, kDppRowHalfMirror, 0xf, 0xf, false);
+        const uint32_t aml = __builtin_amdgcn_update_dpp(0, al, kDppRowHalfMirror, 0xf, 0xf, false);
+        const uint32_t bml = __builtin_amdgcn_update_dpp(0, bl, kDppRowHalfMirror, 0xf, 0xf, false);
+        ph[0] = hi_half ? amh : ah;
+        ph[1] = hi_half ? bmh : bh;
+        ph[2] = hi_half ? ah : amh;
+        ph[3] = hi_half ? bh : bmh;
+        pl[0] = hi_half ? aml : al;
+        pl[1] = hi_half ? bml : bl;
+        pl[2] = hi_half ? al : aml;
+        pl[3] = hi_half ? bl : bml;
       }
       const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int j = 0; j < 4; ++j) {
+        const unsigned long long v = ((unsigned long long)ph[j] << 32) | pl[j];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const uint32_t addr = __builtin_amdgcn_perm(xs[i], base[r], sel[r]);
-          atomicAdd(reinterpret_cast<float*>(sm.tab + addr + kHOff), pi[i]);
+          const uint32_t addr = __builtin_amdgcn_perm(xs[j], base_h[r], sel_h[r]);
+          atomicAdd(reinterpret_cast<unsigned long long*>(lds + addr), v);
         }
       }
     };
 
-    const int my_first = t0 + wave;
-    const int n_my = (my_first < t1) ? (t1 - my_first + WAVES - 1) / WAVES : 0;
-
     // reference maximum: the first tile of every wave
     float m_loc = kNegInf;
     if (n_my > 0) {
-      const u32x4 xk = ntload(reinterpret_cast<const u32x4*>(tile_ptr(my_first)));
-      m_loc = wave_max(score(xk, my_first));
+      const u32x4 xk = ntload(reinterpret_cast<const u32x4*>(tile_ptr(0)));
+      m_loc = wave_max(score(xk, my_first == n_tiles - 1, 0));
     }
     if (lane == 0) sm.vm[wave] = m_loc;
     __syncthreads();
@@ -326,96 +380,101 @@ __global__ void __launch_bounds__(WAVES * 64, 2) decode_kernel(DecodeParams p) {
     __syncthreads();
 
     for (int pass = 0; pass < 2; ++pass) {
-      float lsum = 0.f, smax = kNegInf;
+      float smax = kNegInf;
       bool over = false;
-      auto process = [&](const u32x4 xk, const u32x4 xv, int t) {
-        const float sc = score(xk, t);
+      auto process = [&](const u32x4 xk, const u32x4 xv, int i) {
+        const bool masked = (my_first + i * WAVES) == n_tiles - 1;   // only the globally last tile is partial
+        const float sc = score(xk, masked, i);
         smax = fmaxf(smax, sc);
         const float e = sc - m_ref;
         over |= e > kThr;
-        const float pp = __builtin_amdgcn_exp2f(fminf(e, kThr));
-        lsum += (NG == 32 && (u & 1)) ? 0.f : pp;
-        accum_v(xv, pp);
+        accum_v(xv, __builtin_amdgcn_exp2f(fminf(e, kThr)));
       };
-      // rotating prefetch of kPF tiles per wave (K and V index blocks)
       constexpr int kPF = 4;
-      u32x4 bk[kPF], bv[kPF];
       if (n_my > 0) {
-#pragma unroll
-      for (int j = 0; j < kPF; ++j) {
-        const uint8_t* pa = tile_ptr(my_first + (j < n_my ? j : n_my - 1) * WAVES);
-        bk[j] = ntload(reinterpret_cast<const u32x4*>(pa));
-        bv[j] = ntload(reinterpret_cast<const u32x4*>(pa + p.kind_bytes));
-      }
-      // steady state: branch-free, every slot is refilled (clamped to the last tile, so the
-      // refills past the end re-read a valid tile and are never consumed)
-      const int n_full = n_my - n_my % kPF;
-      for (int i0 = 0; i0 < n_full; i0 += kPF) {
+        u32x4 bk[kPF], bv[kPF];
 #pragma unroll
         for (int j = 0; j < kPF; ++j) {
-          // keep each slot's work in program order: hoisting a later slot's index
-          // arithmetic above this point would stall on that slot's in-flight load
-          __builtin_amdgcn_sched_barrier(0);
-          process(bk[j], bv[j], my_first + (i0 + j) * WAVES);
-          const int inext = (i0 + j + kPF < n_my) ? (i0 + j + kPF) : (n_my - 1);
-          const uint8_t* pa = tile_ptr(my_first + inext * WAVES);
+          const uint8_t* pa = tile_ptr(j < n_my ? j : n_my - 1);
           bk[j] = ntload(reinterpret_cast<const u32x4*>(pa));
           bv[j] = ntload(reinterpret_cast<const u32x4*>(pa + p.kind_bytes));
         }
-      }
+        // steady state: branch-free, every slot refilled (clamped to the last tile; refills
+        // past the end re-read a valid tile and are never consumed)
+        const int n_full = n_my - n_my % kPF;
+        for (int i0 = 0; i0 < n_full; i0 += kPF) {
 #pragma unroll
-      for (int j = 0; j < kPF - 1; ++j)
-        if (n_full + j < n_my) process(bk[j], bv[j], my_first + (n_full + j) * WAVES);
+          for (int j = 0; j < kPF; ++j) {
+            // keep each slot's work in program order: hoisting a later slot's index
+            // arithmetic above this point would stall on that slot's in-flight load
+            __builtin_amdgcn_sched_barrier(0);
+            process(bk[j], bv[j], i0 + j);
+            const int inext = (i0 + j + kPF < n_my) ? (i0 + j + kPF) : (n_my - 1);
+            const uint8_t* pa = tile_ptr(inext);
+            bk[j] = ntload(reinterpret_cast<const u32x4*>(pa));
+            bv[j] = ntload(reinterpret_cast<const u32x4*>(pa + p.kind_bytes));
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kPF - 1; ++j)
+          if (n_full + j < n_my) process(bk[j], bv[j], n_full + j);
       }
-      lsum = wave_sum(lsum);
       smax = wave_max(smax);
       const bool wover = __any(over);
       if (lane == 0) {
-        sm.vl[wave] = lsum;
         sm.vm[wave] = smax;
         sm.vover[wave] = wover ? 1 : 0;
       }
       __syncthreads();
       int any_over = 0;
       float all_max = kNegInf;
-      l_vq = 0.f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
         any_over |= sm.vover[w];
         all_max = fmaxf(all_max, sm.vm[w]);
-        l_vq += sm.vl[w];
       }
       if (!any_over || pass == 1) break;
-      // rare: a score exceeded the reference by more than 2^64; redo with the exact maximum
+      // rare: a score exceeded the reference by more than 17; redo with the exact maximum
       m_ref = all_max;
       __syncthreads();
-      for (int e = tid; e < kCodes * 32; e += NT)
-        reinterpret_cast<float*>(sm.tab + (e >> 5) * kRowBytes + kHOff)[e & 31] = 0.f;
+      u32x4* hz = reinterpret_cast<u32x4*>(sm.hist);
+      for (int e = tid; e < kCodes * 32 * 8 / 16; e += NT) hz[e] = u32x4{0u, 0u, 0u, 0u};
       __syncthreads();
     }
   }
 
   // ---- 5. value contraction o_vq = H^T Cv_tau, merge, write -----------------------------
   constexpr int PARTS = NT / D;
-  float o_vq = 0.f;
+  float o_vq = 0.f, l_vq = 0.f;
   if (has_vq) {
     const int ch = tid % D, part = tid / D, g = ch / C;
     const uint16_t* sv = p.cbv + ((int64_t)h * p.G + p.tau) * kCodes * D + ch;
     float acc = 0.f;
 #pragma unroll 16
     for (int k = part; k < kCodes; k += PARTS) {
-      const float* row = reinterpret_cast<const float*>(sm.tab + k * kRowBytes + kHOff);
-      float hk = row[g];
-      if constexpr (NG == 16) hk += row[16 + g];
+      const unsigned long long hv = sm.hist[k * 32 + g];
+      const float hk = fmaf((float)(uint32_t)(hv >> 32), 4294967296.f, (float)(uint32_t)hv);
       acc = fmaf(hk, bf16_at(sv + k * D), acc);
     }
     sm.red[tid] = acc;
+  }
+  __syncthreads();
+  if (has_vq && tid < 64) {
+    // normaliser: the quantised weights of group 0 sum to l * 2^30
+    unsigned long long t = 0;
+#pragma unroll
+    for (int k = tid; k < kCodes; k += 64) t += sm.hist[k * 32];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) t += __shfl_xor(t, m, 64);
+    if (tid == 0) sm.vm[0] = fmaf((float)(uint32_t)(t >> 32), 4294967296.f, (float)(uint32_t)t) * (1.f / kFix);
   }
   __syncthreads();
   if (tid < D) {
     if (has_vq) {
 #pragma unroll
       for (int pp = 0; pp < PARTS; ++pp) o_vq += sm.red[pp * D + tid];
+      o_vq *= 1.f / kFix;
+      l_vq = sm.vm[0];
     }
     const bool vq_live = has_vq && l_vq > 0.f;
     float M = vq_live ? m_ref : kNegInf;
@@ -472,9 +531,8 @@ __global__ void __launch_bounds__(D) combine_kernel(DecodeParams p) {
 
 template <int NG, int C>
 hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
-  constexpr int WAVES = 4;
   const int Q = p.B * p.Hq;
-  hipLaunchKernelGGL((decode_kernel<NG, C, WAVES>), dim3(Q * p.S), dim3(WAVES * 64), 0, stream, p);
+  hipLaunchKernelGGL((decode_kernel<NG, C, kWaves>), dim3(Q * p.S), dim3(kWaves * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
   hipLaunchKernelGGL((combine_kernel<NG * C>), dim3(Q), dim3(NG * C), 0, stream, p);
@@ -482,6 +540,11 @@ hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Largest number of vector-quantized tokens one split may cover: keeps every 64-bit histogram
+// sum below 2^64 (one token adds at most 2^47) and a wave's tiles within its page-id vector
+// (256 tiles per wave x 8 waves).
+int decode_max_split_tokens(int ng) { return ng == 32 ? 65536 : 65536; }
 
 hipError_t launch_decode(const DecodeParams& p, int ng, int c, hipStream_t stream) {
   if (ng == 32 && c == 4) return launch_variant<32, 4>(p, stream);
