@@ -43,6 +43,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace lvq {
 namespace {
 
@@ -50,15 +52,15 @@ constexpr int kRowBytes = 256;
 constexpr float kThr = 17.f;            // p <= 2^17 before a redo is forced
 constexpr float kFix = 1073741824.f;    // 2^30: fixed-point scale of the histogram
 constexpr float kNegInf = -INFINITY;
-constexpr int kWaves = 8;
-constexpr int kMaxTilesPerWave = 256;   // page-id vector: 4 VGPRs of 64 lanes
+constexpr int kWaves = 16;
+constexpr int kMaxTilesPerWave = 128;   // page-id vector: 2 VGPRs of 64 lanes
 
 template <int D, int WAVES>
 struct DecodeSmem {
   uint8_t lut[kCodes * kRowBytes];              // [0, 64K): LUT rows (must stay first)
   unsigned long long hist[kCodes * 32];         // [64K, 128K): u64 histogram rows
   float q[D];                                   // q' (log2 units)
-  float red[WAVES * 64 > D ? WAVES * 64 : D];   // raw q, then contraction partials
+  float red[2 * WAVES * 64];                    // raw q, then contraction partials
   float wo[WAVES][D];                           // window partial o per wave
   float wm[WAVES], wl[WAVES];                   // window partial max / sum per wave
   float vm[WAVES];                              // VQ max per wave
@@ -86,8 +88,12 @@ __global__ void __launch_bounds__(WAVES * 64, 1) decode_kernel(DecodeParams p) {
   constexpr int TW = 256 / G4;      // tokens per wave tile (1 KB of 8-bit indices)
   constexpr int NT = WAVES * 64;
   constexpr int CPL = D / 64;       // window channels per lane
+  constexpr int LPT = kCodes * NG / NT;   // LUT entries built per thread
+  constexpr int NPG = kMaxTilesPerWave / 64;
   static_assert(NG == 16 || NG == 32, "NG");
   static_assert(CPL == 1 || CPL == 2 || CPL == 4, "D");
+  static_assert(LPT >= 1 && NT % NG == 0, "LUT build mapping");
+  using SliceT = typename std::conditional<C == 4, uint2, uint4>::type;
 
   __shared__ DecodeSmem<D, WAVES> sm;
   uint8_t* const lds = sm.lut;      // LDS address 0 (histogram at 65536)
@@ -119,42 +125,99 @@ __global__ void __launch_bounds__(WAVES * 64, 1) decode_kernel(DecodeParams p) {
   const int t1 = (int)(((int64_t)n_tiles * (s + 1)) / p.S);
   const bool has_vq = t1 > t0;
 
-  // ---- 1. q' = scale*log2(e) * R^T q -------------------------------------------------
-  float* qraw = sm.red;
-  if (tid < D) qraw[tid] = bf16_at(p.q + (int64_t)qi * D + tid);
-  __syncthreads();
-  if (tid < D) {
-    float v;
-    if (p.rot) {
-      v = 0.f;
-      for (int i = 0; i < D; ++i) v = fmaf(p.rot[i * D + tid], qraw[i], v);
-    } else {
-      v = qraw[tid];
+  // ---- 0. issue the first global loads: page ids, the first index tiles, the key
+  //         codebook slice and q, so their latency overlaps the prologue -------------
+  const int Qd = lane / G4, u = lane % G4;
+  const uint8_t* pool_h = has_vq ? p.pool_lj + (int64_t)h * p.head_stride + lane * 16 : nullptr;
+  const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
+  const int pt_mask = (1 << p.pt_shift) - 1;
+  const int my_first = t0 + wave;
+  const int n_my = (has_vq && my_first < t1) ? (t1 - my_first + WAVES - 1) / WAVES : 0;
+
+  // page ids of this wave's tiles: lane l of pg[c] holds the page of tile 64*c + l
+  int pg[NPG];
+#pragma unroll
+  for (int c = 0; c < NPG; ++c) {
+    const int i = 64 * c + lane;
+    int v = 0;
+    if (i < n_my) {
+      v = bt[((my_first + i * WAVES) * TW) >> p.pt_shift];
+      v = (v < 0 || v >= p.num_pages) ? 0 : v;
     }
-    sm.q[tid] = v * p.scale_log2;
+    pg[c] = v;
+  }
+  auto tile_ptr = [&](int i) -> const uint8_t* {   // i: wave-uniform tile ordinal
+    const int c = i >> 6, l = i & 63;
+    int page = __builtin_amdgcn_readlane(pg[0], l);
+#pragma unroll
+    for (int cc = 1; cc < NPG; ++cc) {
+      const int pc = __builtin_amdgcn_readlane(pg[cc], l);
+      page = c == cc ? pc : page;
+    }
+    const int u0 = (my_first + i * WAVES) * TW;
+    return pool_h + (int64_t)page * p.page_bytes + (int64_t)(u0 & pt_mask) * NG;
+  };
+  constexpr int kPF = 2;
+  u32x4 bk[kPF], bv[kPF];
+  auto load_first = [&]() {
+#pragma unroll
+    for (int j = 0; j < kPF; ++j) {
+      const uint8_t* pa = tile_ptr(j < n_my ? j : n_my - 1);
+      bk[j] = ntload(reinterpret_cast<const u32x4*>(pa));
+      bv[j] = ntload(reinterpret_cast<const u32x4*>(pa + p.kind_bytes));
+    }
+  };
+  if (n_my > 0) load_first();
+
+  const int g_lut = tid % NG;   // fixed per thread
+  SliceT ks[LPT];
+  if (has_vq) {
+    const uint16_t* sk = p.cbk + ((int64_t)h * p.G + p.tau) * kCodes * D + g_lut * C;
+#pragma unroll
+    for (int m = 0; m < LPT; ++m) ks[m] = *reinterpret_cast<const SliceT*>(sk + ((tid + m * NT) / NG) * D);
+  }
+  const float qraw = tid < D ? bf16_at(p.q + (int64_t)qi * D + tid) : 0.f;
+
+  // ---- 1. q' = scale*log2(e) * R^T q -------------------------------------------------
+  if (tid < D) sm.red[tid] = qraw;
+  __syncthreads();
+  if (p.rot) {
+    constexpr int RP = NT / D;            // partial sums per output channel
+    const int j = tid % D, part = tid / D;
+    float v = 0.f;
+#pragma unroll 8
+    for (int i = part * (D / RP); i < (part + 1) * (D / RP); ++i) v = fmaf(p.rot[i * D + j], sm.red[i], v);
+    float* parts = &sm.wo[0][0];          // NT floats of scratch (window partials come later)
+    parts[part * D + j] = v;
+    __syncthreads();
+    if (tid < D) {
+      float t = 0.f;
+#pragma unroll
+      for (int pp = 0; pp < RP; ++pp) t += parts[pp * D + tid];
+      sm.q[tid] = t * p.scale_log2;
+    }
+  } else if (tid < D) {
+    sm.q[tid] = qraw * p.scale_log2;
   }
   __syncthreads();
 
   // ---- 2. lookup table and zeroed histogram ---------------------------------------------
   if (has_vq) {
-    const uint16_t* sk = p.cbk + ((int64_t)h * p.G + p.tau) * kCodes * D;
-    const int g = tid % NG;               // fixed per thread (NT is a multiple of NG)
     float qg[C];
 #pragma unroll
-    for (int i = 0; i < C; ++i) qg[i] = sm.q[g * C + i];
-#pragma unroll 4
-    for (int e = tid; e < kCodes * NG; e += NT) {
-      const int k = e / NG;
-      const uint16_t* src = sk + k * D + g * C;
+    for (int i = 0; i < C; ++i) qg[i] = sm.q[g_lut * C + i];
+#pragma unroll
+    for (int m = 0; m < LPT; ++m) {
+      const int k = (tid + m * NT) / NG;
       float acc = 0.f;
       if constexpr (C == 4) {
-        const uint2 w = *reinterpret_cast<const uint2*>(src);
+        const uint2 w = ks[m];
         acc = fmaf(qg[0], bf16_lo(w.x), acc);
         acc = fmaf(qg[1], bf16_hi(w.x), acc);
         acc = fmaf(qg[2], bf16_lo(w.y), acc);
         acc = fmaf(qg[3], bf16_hi(w.y), acc);
       } else {
-        const uint4 w = *reinterpret_cast<const uint4*>(src);
+        const uint4 w = ks[m];
         acc = fmaf(qg[0], bf16_lo(w.x), acc);
         acc = fmaf(qg[1], bf16_hi(w.x), acc);
         acc = fmaf(qg[2], bf16_lo(w.y), acc);
@@ -165,74 +228,73 @@ __global__ void __launch_bounds__(WAVES * 64, 1) decode_kernel(DecodeParams p) {
         acc = fmaf(qg[7], bf16_hi(w.w), acc);
       }
       float* row = reinterpret_cast<float*>(lds + k * kRowBytes);
-      row[g] = acc;
-      if constexpr (NG == 16) row[16 + g] = acc;
+      row[g_lut] = acc;
+      if constexpr (NG == 16) row[16 + g_lut] = acc;
     }
     u32x4* hz = reinterpret_cast<u32x4*>(sm.hist);
     for (int e = tid; e < kCodes * 32 * 8 / 16; e += NT) hz[e] = u32x4{0u, 0u, 0u, 0u};
   }
 
-  // ---- 3. bf16 window rows (prefix + recent) of this split ------------------------------
+  // ---- 3. bf16 window rows (prefix + recent) of this split: one token per wave at a
+  //         time, lanes over channels, four tokens' loads in flight -------------------
   float m_w = kNegInf, l_w = 0.f, o_w[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) o_w[c] = 0.f;
   {
     const int64_t pre_row0 = ((int64_t)b * p.Hkv + h) * p.P;
     const int64_t rec_row0 = ((int64_t)b * p.Hkv + h) * p.R;
-    for (int cbase = w0 + wave * 64; cbase < w1; cbase += NT) {
-      const int w = cbase + lane;
-      const bool ok = w < w1;
-      float sc = kNegInf;
-      if (ok) {
-        const uint16_t* kr = (w < n_prefix) ? p.k_prefix + (pre_row0 + w) * D
-                                            : p.k_recent + (rec_row0 + (w - n_prefix)) * D;
-        float acc = 0.f;
+    float qc[CPL];
 #pragma unroll
-        for (int c8 = 0; c8 < D / 8; ++c8) {
-          const uint4 kv = *reinterpret_cast<const uint4*>(kr + c8 * 8);
-          const float* qq = sm.q + c8 * 8;
-          acc = fmaf(qq[0], bf16_lo(kv.x), acc);
-          acc = fmaf(qq[1], bf16_hi(kv.x), acc);
-          acc = fmaf(qq[2], bf16_lo(kv.y), acc);
-          acc = fmaf(qq[3], bf16_hi(kv.y), acc);
-          acc = fmaf(qq[4], bf16_lo(kv.z), acc);
-          acc = fmaf(qq[5], bf16_hi(kv.z), acc);
-          acc = fmaf(qq[6], bf16_lo(kv.w), acc);
-          acc = fmaf(qq[7], bf16_hi(kv.w), acc);
-        }
-        sc = acc;
+    for (int c = 0; c < CPL; ++c) qc[c] = sm.q[lane * CPL + c];
+    auto row_of = [&](const uint16_t* pre, const uint16_t* rec, int w) -> const uint16_t* {
+      return (w < n_prefix) ? pre + (pre_row0 + w) * D : rec + (rec_row0 + (w - n_prefix)) * D;
+    };
+    auto load_ch = [&](const uint16_t* row, float* dst) {
+      if constexpr (CPL == 1) {
+        dst[0] = bf16_at(row + lane);
+      } else if constexpr (CPL == 2) {
+        const uint32_t v2 = *reinterpret_cast<const uint32_t*>(row + 2 * lane);
+        dst[0] = bf16_lo(v2);
+        dst[1] = bf16_hi(v2);
+      } else {
+        const uint2 v4 = *reinterpret_cast<const uint2*>(row + 4 * lane);
+        dst[0] = bf16_lo(v4.x);
+        dst[1] = bf16_hi(v4.x);
+        dst[2] = bf16_lo(v4.y);
+        dst[3] = bf16_hi(v4.y);
       }
-      const float mc = wave_max(sc);
-      const float mn = fmaxf(m_w, mc);
-      const float a = __builtin_amdgcn_exp2f(m_w - mn);
-      const float pn = ok ? __builtin_amdgcn_exp2f(sc - mn) : 0.f;
-      l_w = l_w * a + wave_sum(pn);
+    };
+    constexpr int WU = 4;
+    for (int wb = w0 + wave; wb < w1; wb += WAVES * WU) {
+      float kx[WU][CPL], vx[WU][CPL];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) o_w[c] *= a;
-      m_w = mn;
-      const int cnt = (w1 - cbase) < 64 ? (w1 - cbase) : 64;
-#pragma unroll 8
-      for (int n = 0; n < cnt; ++n) {
-        const float pv = __shfl(pn, n, 64);
-        const int wn = cbase + n;
-        const uint16_t* vr = (wn < n_prefix) ? p.v_prefix + (pre_row0 + wn) * D
-                                             : p.v_recent + (rec_row0 + (wn - n_prefix)) * D;
-        if constexpr (CPL == 1) {
-          o_w[0] = fmaf(pv, bf16_at(vr + lane), o_w[0]);
-        } else if constexpr (CPL == 2) {
-          const uint32_t v2 = *reinterpret_cast<const uint32_t*>(vr + 2 * lane);
-          o_w[0] = fmaf(pv, bf16_lo(v2), o_w[0]);
-          o_w[1] = fmaf(pv, bf16_hi(v2), o_w[1]);
-        } else {
-          const uint2 v4 = *reinterpret_cast<const uint2*>(vr + 4 * lane);
-          o_w[0] = fmaf(pv, bf16_lo(v4.x), o_w[0]);
-          o_w[1] = fmaf(pv, bf16_hi(v4.x), o_w[1]);
-          o_w[2] = fmaf(pv, bf16_lo(v4.y), o_w[2]);
-          o_w[3] = fmaf(pv, bf16_hi(v4.y), o_w[3]);
+      for (int j = 0; j < WU; ++j) {
+        const int w = wb + j * WAVES;
+        if (w < w1) {
+          load_ch(row_of(p.k_prefix, p.k_recent, w), kx[j]);
+          load_ch(row_of(p.v_prefix, p.v_recent, w), vx[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < WU; ++j) {
+        const int w = wb + j * WAVES;
+        if (w < w1) {
+          float d = 0.f;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) d = fmaf(qc[c], kx[j][c], d);
+          d = wave_sum(d);
+          const float mn = fmaxf(m_w, d);
+          const float a = __builtin_amdgcn_exp2f(m_w - mn);
+          const float pw = __builtin_amdgcn_exp2f(d - mn);
+          l_w = fmaf(l_w, a, pw);
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) o_w[c] = fmaf(o_w[c], a, pw * vx[j][c]);
+          m_w = mn;
         }
       }
     }
   }
+  // all threads finished the rotation scratch reads (barrier after q') before these writes
   if (lane == 0) {
     sm.wm[wave] = m_w;
     sm.wl[wave] = l_w;
@@ -245,7 +307,6 @@ __global__ void __launch_bounds__(WAVES * 64, 1) decode_kernel(DecodeParams p) {
   // ---- 4. vector-quantized rows ---------------------------------------------------------
   float m_ref = kNegInf;
   if (has_vq) {
-    const int Qd = lane / G4, u = lane % G4;
     uint32_t base_l[4], sel_l[4], base_h[4], sel_h[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -258,34 +319,6 @@ __global__ void __launch_bounds__(WAVES * 64, 1) decode_kernel(DecodeParams p) {
     }
     const int tok = (NG == 16) ? u : (((u >= 4) ? 2 : 0) + ((u & 2) ? 1 : 0));
     const bool hi_half = (u >= 4);
-    const uint8_t* pool_h = p.pool_lj + (int64_t)h * p.head_stride + lane * 16;
-    const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
-    const int pt_mask = (1 << p.pt_shift) - 1;
-
-    const int my_first = t0 + wave;
-    const int n_my = (my_first < t1) ? (t1 - my_first + WAVES - 1) / WAVES : 0;
-
-    // page ids of this wave's tiles: lane l of pg[c] holds the page of tile 64*c + l
-    int pg[kMaxTilesPerWave / 64];
-#pragma unroll
-    for (int c = 0; c < kMaxTilesPerWave / 64; ++c) {
-      const int i = 64 * c + lane;
-      int v = 0;
-      if (i < n_my) {
-        v = bt[((my_first + i * WAVES) * TW) >> p.pt_shift];
-        v = (v < 0 || v >= p.num_pages) ? 0 : v;
-      }
-      pg[c] = v;
-    }
-    auto tile_ptr = [&](int i) -> const uint8_t* {   // i: wave-uniform tile ordinal
-      const int c = i >> 6, l = i & 63;
-      const int p0 = __builtin_amdgcn_readlane(pg[0], l), p1 = __builtin_amdgcn_readlane(pg[1], l);
-      const int p2 = __builtin_amdgcn_readlane(pg[2], l), p3 = __builtin_amdgcn_readlane(pg[3], l);
-      const int page = c == 0 ? p0 : (c == 1 ? p1 : (c == 2 ? p2 : p3));
-      const int u0 = (my_first + i * WAVES) * TW;
-      return pool_h + (int64_t)page * p.page_bytes + (int64_t)(u0 & pt_mask) * NG;
-    };
-
     auto score = [&](const u32x4 xk, bool masked, int i) -> float {
       const uint32_t xs[4] = {xk.x, xk.y, xk.z, xk.w};
       float acc[4];
@@ -366,12 +399,9 @@ __global__ void __launch_bounds__(WAVES * 64, 1) decode_kernel(DecodeParams p) {
       }
     };
 
-    // reference maximum: the first tile of every wave
+    // reference maximum: the first tile of every wave (already in flight)
     float m_loc = kNegInf;
-    if (n_my > 0) {
-      const u32x4 xk = ntload(reinterpret_cast<const u32x4*>(tile_ptr(0)));
-      m_loc = wave_max(score(xk, my_first == n_tiles - 1, 0));
-    }
+    if (n_my > 0) m_loc = wave_max(score(bk[0], my_first == n_tiles - 1, 0));
     if (lane == 0) sm.vm[wave] = m_loc;
     __syncthreads();
     m_ref = sm.vm[0];
@@ -390,15 +420,8 @@ __global__ void __launch_bounds__(WAVES * 64, 1) decode_kernel(DecodeParams p) {
         over |= e > kThr;
         accum_v(xv, __builtin_amdgcn_exp2f(fminf(e, kThr)));
       };
-      constexpr int kPF = 4;
       if (n_my > 0) {
-        u32x4 bk[kPF], bv[kPF];
-#pragma unroll
-        for (int j = 0; j < kPF; ++j) {
-          const uint8_t* pa = tile_ptr(j < n_my ? j : n_my - 1);
-          bk[j] = ntload(reinterpret_cast<const u32x4*>(pa));
-          bv[j] = ntload(reinterpret_cast<const u32x4*>(pa + p.kind_bytes));
-        }
+        if (pass > 0) load_first();
         // steady state: branch-free, every slot refilled (clamped to the last tile; refills
         // past the end re-read a valid tile and are never consumed)
         const int n_full = n_my - n_my % kPF;
@@ -444,19 +467,28 @@ __global__ void __launch_bounds__(WAVES * 64, 1) decode_kernel(DecodeParams p) {
   }
 
   // ---- 5. value contraction o_vq = H^T Cv_tau, merge, write -----------------------------
-  constexpr int PARTS = NT / D;
+  // thread -> (channel pair cp, codeword part); each part sums KPT codewords
+  constexpr int CP = D / 2;
+  constexpr int PARTS = NT / CP;
+  constexpr int KPT = kCodes / PARTS;
+  static_assert(NT % CP == 0 && kCodes % PARTS == 0, "contraction mapping");
   float o_vq = 0.f, l_vq = 0.f;
   if (has_vq) {
-    const int ch = tid % D, part = tid / D, g = ch / C;
-    const uint16_t* sv = p.cbv + ((int64_t)h * p.G + p.tau) * kCodes * D + ch;
-    float acc = 0.f;
-#pragma unroll 16
-    for (int k = part; k < kCodes; k += PARTS) {
-      const unsigned long long hv = sm.hist[k * 32 + g];
+    const int cp = tid % CP, part = tid / CP, g = (2 * cp) / C;
+    const uint16_t* sv = p.cbv + ((int64_t)h * p.G + p.tau) * kCodes * D + 2 * cp;
+    uint32_t cv[KPT];
+#pragma unroll
+    for (int m = 0; m < KPT; ++m) cv[m] = *reinterpret_cast<const uint32_t*>(sv + (part + m * PARTS) * D);
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int m = 0; m < KPT; ++m) {
+      const unsigned long long hv = sm.hist[(part + m * PARTS) * 32 + g];
       const float hk = fmaf((float)(uint32_t)(hv >> 32), 4294967296.f, (float)(uint32_t)hv);
-      acc = fmaf(hk, bf16_at(sv + k * D), acc);
+      a0 = fmaf(hk, bf16_lo(cv[m]), a0);
+      a1 = fmaf(hk, bf16_hi(cv[m]), a1);
     }
-    sm.red[tid] = acc;
+    sm.red[part * D + 2 * cp] = a0;
+    sm.red[part * D + 2 * cp + 1] = a1;
   }
   __syncthreads();
   if (has_vq && tid < 64) {
