@@ -95,19 +95,22 @@ Sizes sizes_of(const loopvq_config* c) {
 // Tokens per wave tile of the decode kernel (1 KB of 8-bit indices).
 int decode_tile_tokens(const loopvq_config* c) { return 256 / ((c->head_dim / c->chans_per_group) / 4); }
 
-// Fewest splits the decode kernel accepts: one split covers at most 2040 tiles (a wave
-// walks at most 255 of them, and the 64-bit value histogram cannot overflow).
+// Fewest splits the decode kernel accepts: one split covers at most 2048 tiles at NG=32
+// (16 waves x 128) or 1024 at NG=16 (8 waves x 128) -- the page ids a wave keeps in two
+// VGPRs -- i.e. at most 65536 vector-quantized tokens, so the 64-bit value histogram (each
+// token adds at most 2^47) cannot overflow.
 int min_splits(const loopvq_config* c, int32_t max_seq_len) {
   const int64_t n_vq = std::max<int64_t>(0, int64_t(max_seq_len) - c->prefix_tokens - c->recent_tokens);
   const int64_t tiles = (n_vq + decode_tile_tokens(c) - 1) / decode_tile_tokens(c);
-  return (int)std::max<int64_t>(1, (tiles + 2039) / 2040);
+  const int64_t max_tiles = (c->head_dim / c->chans_per_group) == 32 ? 2048 : 1024;
+  return (int)std::max<int64_t>(1, (tiles + max_tiles - 1) / max_tiles);
 }
 
 int plan_splits(const loopvq_config* c, int32_t batch, int32_t max_seq_len) {
   const int64_t Q = int64_t(batch) * c->num_q_heads;
   const int64_t n_vq = std::max<int64_t>(0, int64_t(max_seq_len) - c->prefix_tokens - c->recent_tokens);
   const int64_t tiles = (n_vq + decode_tile_tokens(c) - 1) / decode_tile_tokens(c);
-  const int64_t slots = 256;  // one resident decode workgroup per CU
+  const int64_t slots = (c->head_dim / c->chans_per_group) == 32 ? 256 : 512;  // resident workgroups
   int64_t S = Q >= slots ? 1 : (slots + Q - 1) / Q;
   const int64_t max_by_work = std::max<int64_t>(1, tiles / 32);   // >= 32 tiles per split
   S = std::min(S, max_by_work);

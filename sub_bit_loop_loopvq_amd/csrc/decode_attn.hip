@@ -16,7 +16,8 @@
 //  * LDS layout, [0, 64K): one 256-byte row per codeword k holding LUT[k][g] at
 //    byte 4*g (NG=32) or two copies at 4*g and 64 + 4*g (NG=16, so the 64 lanes
 //    of a read cover all 32 banks).  [64K, 128K): the value histogram, one
-//    256-byte row per codeword, H[k][g] as a 64-bit integer at byte 8*g.  The
+//    256-byte row per codeword, H[k][g] as a 64-bit integer (slots permuted so a
+//    half-wave's updates hit distinct bank pairs).  The
 //    address of either entry is (region byte, index byte, group byte): one
 //    v_perm_b32 merges the packed index byte with two constant bytes, so an
 //    index costs one VALU op plus one LDS op.
@@ -52,13 +53,18 @@ constexpr int kRowBytes = 256;
 constexpr float kThr = 17.f;            // p <= 2^17 before a redo is forced
 constexpr float kFix = 1073741824.f;    // 2^30: fixed-point scale of the histogram
 constexpr float kNegInf = -INFINITY;
-constexpr int kWaves = 16;
 constexpr int kMaxTilesPerWave = 128;   // page-id vector: 2 VGPRs of 64 lanes
 
-template <int D, int WAVES>
+// Waves per workgroup.  NG=32 needs a separate 64 KB histogram region (128 KB+ of LDS, one
+// workgroup per CU, 16 waves); at NG=16 the histogram fits in the unused half of the LUT
+// rows (~72 KB, two workgroups per CU, 8 waves each).
+template <int NG>
+constexpr int waves_for() { return NG == 32 ? 16 : 8; }
+
+template <int NG, int D, int WAVES>
 struct DecodeSmem {
-  uint8_t lut[kCodes * kRowBytes];              // [0, 64K): LUT rows (must stay first)
-  unsigned long long hist[kCodes * 32];         // [64K, 128K): u64 histogram rows
+  uint8_t tab[kCodes * kRowBytes];              // [0, 64K): LUT rows (must stay first)
+  unsigned long long hist[NG == 32 ? kCodes * 32 : 2];   // [64K, 128K) at NG=32: histogram rows
   float q[D];                                   // q' (log2 units)
   float red[2 * WAVES * 64];                    // raw q, then contraction partials
   float wo[WAVES][D];                           // window partial o per wave
@@ -66,6 +72,10 @@ struct DecodeSmem {
   float vm[WAVES];                              // VQ max per wave
   int vover[WAVES];
 };
+
+// Byte offset (from LDS address 0) of histogram entry (k, g).
+template <int NG>
+__device__ __forceinline__ uint32_t hist_off(uint32_t k, uint32_t g);
 
 __device__ __forceinline__ u32x4 ntload(const u32x4* ptr) { return __builtin_nontemporal_load(ptr); }
 
@@ -81,8 +91,35 @@ __device__ __forceinline__ void to_fixed(float p, uint32_t& hi, uint32_t& lo) {
   lo = (uint32_t)lf;
 }
 
+// Slot of group g inside a 32-entry histogram row.  A 64-bit atomic touches two banks; at
+// NG=32 groups g and g+16 would share a bank pair, so the slot is permuted such that the 16
+// groups a half-wave of lanes updates together (4u + rr, u < 8, two consecutive rr) land on
+// 16 distinct bank pairs.
+template <int NG>
+__device__ __forceinline__ uint32_t hist_slot(uint32_t g) {
+  if constexpr (NG == 32) return 2u * (g >> 2) + (g & 1u) + 16u * ((g >> 1) & 1u);
+  return g;
+}
+
+template <int NG>
+__device__ __forceinline__ uint32_t hist_off(uint32_t k, uint32_t g) {
+  if constexpr (NG == 32) return 65536u + k * kRowBytes + hist_slot<NG>(g) * 8u;
+  return k * kRowBytes + 128u + g * 8u;
+}
+
+template <int NG, int D, int WAVES>
+__device__ __forceinline__ void zero_hist(DecodeSmem<NG, D, WAVES>& sm, int tid) {
+  if constexpr (NG == 32) {
+    u32x4* hz = reinterpret_cast<u32x4*>(sm.hist);
+    for (int e = tid; e < kCodes * 32 * 8 / 16; e += WAVES * 64) hz[e] = u32x4{0u, 0u, 0u, 0u};
+  } else {
+    for (int e = tid; e < kCodes * 8; e += WAVES * 64)    // 8 x 16 B per row, bytes [128, 256)
+      *reinterpret_cast<u32x4*>(sm.tab + (e >> 3) * kRowBytes + 128 + (e & 7) * 16) = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
 template <int NG, int C, int WAVES>
-__global__ void __launch_bounds__(WAVES * 64, 1) decode_kernel(DecodeParams p) {
+__global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
   constexpr int D = NG * C;
   constexpr int G4 = NG / 4;        // lanes that share a token quad
   constexpr int TW = 256 / G4;      // tokens per wave tile (1 KB of 8-bit indices)
@@ -95,8 +132,8 @@ __global__ void __launch_bounds__(WAVES * 64, 1) decode_kernel(DecodeParams p) {
   static_assert(LPT >= 1 && NT % NG == 0, "LUT build mapping");
   using SliceT = typename std::conditional<C == 4, uint2, uint4>::type;
 
-  __shared__ DecodeSmem<D, WAVES> sm;
-  uint8_t* const lds = sm.lut;      // LDS address 0 (histogram at 65536)
+  __shared__ DecodeSmem<NG, D, WAVES> sm;
+  uint8_t* const lds = sm.tab;      // LDS address 0
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -157,7 +194,7 @@ __global__ void __launch_bounds__(WAVES * 64, 1) decode_kernel(DecodeParams p) {
     const int u0 = (my_first + i * WAVES) * TW;
     return pool_h + (int64_t)page * p.page_bytes + (int64_t)(u0 & pt_mask) * NG;
   };
-  constexpr int kPF = 2;
+  constexpr int kPF = 4;
   u32x4 bk[kPF], bv[kPF];
   auto load_first = [&]() {
 #pragma unroll
@@ -231,8 +268,7 @@ __global__ void __launch_bounds__(WAVES * 64, 1) decode_kernel(DecodeParams p) {
       row[g_lut] = acc;
       if constexpr (NG == 16) row[16 + g_lut] = acc;
     }
-    u32x4* hz = reinterpret_cast<u32x4*>(sm.hist);
-    for (int e = tid; e < kCodes * 32 * 8 / 16; e += NT) hz[e] = u32x4{0u, 0u, 0u, 0u};
+    zero_hist(sm, tid);
   }
 
   // ---- 3. bf16 window rows (prefix + recent) of this split: one token per wave at a
@@ -312,10 +348,13 @@ __global__ void __launch_bounds__(WAVES * 64, 1) decode_kernel(DecodeParams p) {
     for (int r = 0; r < 4; ++r) {
       const uint32_t rr = (r + Qd) & 3;
       const uint32_t gg = 4u * u + rr;
-      base_l[r] = gg * 4u + ((NG == 16) ? (uint32_t)(Qd & 1) * 64u : 0u);
+      // NG=16: lanes Q and Q+4 share a group, so they read different LUT copies
+      base_l[r] = gg * 4u + ((NG == 16) ? (uint32_t)((Qd >> 2) & 1) * 64u : 0u);
       sel_l[r] = 0x0c0c0000u | ((4u + rr) << 8);             // [0, 0, idx, base.b0]
-      base_h[r] = 0x00010000u | (gg * 8u);
-      sel_h[r] = 0x0c020000u | ((4u + rr) << 8);             // [0, base.b2 = 1, idx, base.b0]
+      const uint32_t ho = hist_off<NG>(0, gg);                  // region and slot bytes
+      base_h[r] = ho;
+      sel_h[r] = (NG == 32) ? (0x0c020000u | ((4u + rr) << 8)) // [0, base.b2 = 1, idx, base.b0]
+                            : (0x0c0c0000u | ((4u + rr) << 8));
     }
     const int tok = (NG == 16) ? u : (((u >= 4) ? 2 : 0) + ((u & 2) ? 1 : 0));
     const bool hi_half = (u >= 4);
@@ -460,8 +499,7 @@ __global__ void __launch_bounds__(WAVES * 64, 1) decode_kernel(DecodeParams p) {
       // rare: a score exceeded the reference by more than 17; redo with the exact maximum
       m_ref = all_max;
       __syncthreads();
-      u32x4* hz = reinterpret_cast<u32x4*>(sm.hist);
-      for (int e = tid; e < kCodes * 32 * 8 / 16; e += NT) hz[e] = u32x4{0u, 0u, 0u, 0u};
+      zero_hist(sm, tid);
       __syncthreads();
     }
   }
@@ -482,7 +520,7 @@ __global__ void __launch_bounds__(WAVES * 64, 1) decode_kernel(DecodeParams p) {
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int m = 0; m < KPT; ++m) {
-      const unsigned long long hv = sm.hist[(part + m * PARTS) * 32 + g];
+      const unsigned long long hv = *reinterpret_cast<const unsigned long long*>(lds + hist_off<NG>(part + m * PARTS, g));
       const float hk = fmaf((float)(uint32_t)(hv >> 32), 4294967296.f, (float)(uint32_t)hv);
       a0 = fmaf(hk, bf16_lo(cv[m]), a0);
       a1 = fmaf(hk, bf16_hi(cv[m]), a1);
@@ -495,7 +533,7 @@ __global__ void __launch_bounds__(WAVES * 64, 1) decode_kernel(DecodeParams p) {
     // normaliser: the quantised weights of group 0 sum to l * 2^30
     unsigned long long t = 0;
 #pragma unroll
-    for (int k = tid; k < kCodes; k += 64) t += sm.hist[k * 32];
+    for (int k = tid; k < kCodes; k += 64) t += *reinterpret_cast<const unsigned long long*>(lds + hist_off<NG>(k, 0));
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) t += __shfl_xor(t, m, 64);
     if (tid == 0) sm.vm[0] = fmaf((float)(uint32_t)(t >> 32), 4294967296.f, (float)(uint32_t)t) * (1.f / kFix);
@@ -564,7 +602,8 @@ __global__ void __launch_bounds__(D) combine_kernel(DecodeParams p) {
 template <int NG, int C>
 hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
   const int Q = p.B * p.Hq;
-  hipLaunchKernelGGL((decode_kernel<NG, C, kWaves>), dim3(Q * p.S), dim3(kWaves * 64), 0, stream, p);
+  constexpr int W = waves_for<NG>();
+  hipLaunchKernelGGL((decode_kernel<NG, C, W>), dim3(Q * p.S), dim3(W * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
   hipLaunchKernelGGL((combine_kernel<NG * C>), dim3(Q), dim3(NG * C), 0, stream, p);
