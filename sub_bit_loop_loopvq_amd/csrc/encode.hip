@@ -8,21 +8,24 @@
 //
 // How (MI355X):
 //  * workgroup = (group range, row block, kv-head); 4 waves; a wave takes one group of
-//    the range at a time and up to 8 tiles of 32 rows.  The host picks the group range:
-//    small batches (tokens leaving the recent window) spread groups over workgroups,
-//    bulk encodes give a workgroup all groups of its rows so whole cache rows are read.
-//  * screen: D_k = ||C_k||^2 + ||x||^2 - 2 x.C_k for a 32-codeword x 32-row tile is two
-//    bf16 32x32x16 MFMAs: the first seeds the accumulator with the two squared norms
-//    (each split exactly into three bf16 parts), the second adds C . (-2x) (the -2 is
-//    exact in bf16).  Each lane holds 128 of its row's 256 distances.
-//  * epilogue: each distance is packed with its codeword index in the low 8 mantissa
-//    bits; a running min and med3 keep the two smallest packed keys (3 VALU ops per
-//    distance).  The two half-waves that share a row are merged.
-//  * exactness: the screen errs by at most delta = 2^-16 (||x||^2 + max_k ||C_k||^2)
-//    and the packing truncates by at most 2^-15 relative.  If the two smallest keys
-//    are further apart than both bounds allow, the screened winner is the exact
-//    argmin.  Otherwise the row's tile is screened again and every codeword within the
-//    bound of the minimum is re-scored as a sequential fp64 sum of squared
+//    the range at a time and up to 4 tiles of 32 rows.  The host picks the group range:
+//    small batches (tokens leaving the recent window) spread groups over workgroups and
+//    read their rows directly; bulk encodes give a workgroup all groups of 128 rows and
+//    stage the rows in LDS, 64 channels at a time, with coalesced LDS-direct loads, so that
+//    every cache line is read from HBM once.
+//  * screen: F_k = x.C_k - (||C_k||^2 + ||x||^2) / 2 = -D_k / 2 for a 32-codeword x
+//    32-row tile is two bf16 32x32x16 MFMAs: the first seeds the accumulator with the two
+//    halved squared norms (each split exactly into three bf16 parts), the second adds
+//    C . x on the raw bf16 operands.  Each lane holds 128 of its row's 256 values.
+//  * epilogue: each value is packed with its codeword index in the low 8 mantissa bits;
+//    the two largest packed keys (the two smallest distances) are kept with max3, med3
+//    and max over pairs of keys: 2.5 VALU ops per distance.  The two half-waves that
+//    share a row are merged.
+//  * exactness: the screen errs by at most delta = 2^-16 (||x||^2 + max_k ||C_k||^2) in
+//    distance and the packing truncates by at most 2^-15 relative.  If the two smallest
+//    distances are further apart than both bounds allow, the screened winner is the
+//    exact argmin.  Otherwise the row's tile is screened again and every codeword within
+//    the bound of the minimum is re-scored as a sequential fp64 sum of squared
 //    differences; the lowest exact minimiser wins (the brute-force definition).
 //  * packing: the 8-bit index is stored as one byte of its 16-index micro-tile
 //    (token quad x group quad) in the page the block table maps its position to.
@@ -33,14 +36,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-
-__device__ __forceinline__ uint32_t neg2_bf16x2(uint32_t w) {
-  // -2 * (two packed bf16); exact: doubling only changes the exponent
-  const float lo = -2.0f * __uint_as_float(w << 16);
-  const float hi = -2.0f * __uint_as_float(w & 0xffff0000u);
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
-}
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) void lds_void;
 
 // v -> (hi, mid, lo) bf16 parts with hi + mid + lo == v to within 2^-24 |v| (truncating splits)
 __device__ __forceinline__ void split3(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
@@ -56,17 +53,45 @@ __device__ __forceinline__ void split3(float v, uint32_t& hi, uint32_t& mid, uin
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-template <int C, int TT>
-__global__ void __launch_bounds__(256) encode_kernel(EncodeParams p, int groups_per_wg) {
+// value of a packed key with its index bits cleared
+__device__ __forceinline__ float key_value(float k) { return __uint_as_float(__float_as_uint(k) & 0xffffff00u); }
+
+// last word of a raw (unstructured, byte-addressed) buffer resource on CDNA
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.  Block L runs
+// on XCD L % 8; give XCD x the contiguous range of logical blocks that starts where the
+// ranges of XCDs 0..x-1 end, so that an XCD works on few kv-heads and its L2 holds their
+// codebooks.  The map is a bijection of [0, n).
+__device__ __forceinline__ int xcd_local_block(int L, int n) {
+  const int x = L & 7, per = n >> 3, rem = n & 7;
+  return x * per + (x < rem ? x : rem) + (L >> 3);
+}
+
+// Bulk stage: channels [ch0, ch0 + 64) of the block's rows for the 4 loop steps, as
+// [loop step t][row r][64 channels] bf16 (128 B per row).  The 8-byte slot s (4 channels) of
+// row r sits at slot s ^ ((r >> 1) & 15) of its row, so the 32 rows that a half-wave reads at
+// one slot fall on 32 distinct 8-byte bank pairs.
+constexpr int kStageCh = 64;
+template <int ROWS>
+__device__ __forceinline__ int stage_off(int r, int t, int s) {
+  return (t * ROWS + r) * 128 + ((s ^ ((r >> 1) & 15)) << 3);
+}
+
+template <int C, int TT, bool STAGE>
+__global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int groups_per_wg, int gx, int gy) {
   constexpr int E = 4 * C;        // sub-vector length (G = 4 loop steps)
   constexpr int NMF = E / 16;     // code MFMAs per distance tile
+  constexpr int ROWS = 32 * TT;   // rows of the block
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, col = lane & 31;
-  const int g0 = blockIdx.x * groups_per_wg;
-  const int row0 = blockIdx.y * (32 * TT);
-  const int h = blockIdx.z;
+  // logical block = (kv-head, row block, group block), kv-head outermost
+  const int q = xcd_local_block(blockIdx.x, gridDim.x);
+  const int g0 = (q % gx) * groups_per_wg;
+  const int row0 = ((q / gx) % gy) * ROWS;
+  const int h = q / (gx * gy);
   const int NG = p.NG;
 
   const uint16_t* cb_h = p.cb_lj + (int64_t)h * NG * kCodes * E;
@@ -75,39 +100,171 @@ __global__ void __launch_bounds__(256) encode_kernel(EncodeParams p, int groups_
   const int pt_mask = (1 << p.pt_shift) - 1;
   const uint32_t one2 = 0x3f803f80u;   // two bf16 ones
   __shared__ u32x4 xrow[4][32][E / 8];  // exact re-rank: the 32 sub-vectors of one tile per wave
+  __shared__ __align__(16) uint8_t stage[STAGE ? 4 * ROWS * 128 : 16];
 
-  for (int g = g0 + wave; g < g0 + groups_per_wg && g < NG; g += 4) {
-    const uint16_t* cb_g = cb_h + (int64_t)g * kCodes * E;
-    const float* nrm_g = nrm_h + g * kCodes;
-
-    // ---- rows of this pass: raw sub-vector elements [16m + 8*half, +8) of row col ----
-    u32x4 xb[TT][NMF];             // -2x, the B operand of the code MFMAs
-    u32x4 bn[TT];                  // B operand of the norm MFMA: [1, 1, 1, |x|^2 parts, 0, 0]
-    float xn[TT];
+  // byte offset (within the kv-head's pool) of each row's micro-tile slot for group 0, or -1
+  // when the row is past the end, its sequence or position is out of range or its page is
+  // unmapped; group g adds (g / 4) * 16 + g % 4.  (All loads are issued unconditionally at
+  // clamped addresses, then validated.)
+  int64_t slot[TT];
+  {
+    int seq[TT], u[TT], page[TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
-      const int r = row0 + tt * 32 + col;
-      const bool ok = r < p.n_tokens;
-      const uint16_t* base = p.src + (int64_t)r * p.stride_token + (int64_t)h * p.stride_head;
+      const int r = min(row0 + tt * 32 + col, p.n_tokens - 1);
+      seq[tt] = p.seq_id[r];
+      u[tt] = p.vq_pos[r];
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int sq = min(max(seq[tt], 0), p.batch - 1);
+      const int pg = min(max(u[tt] >> p.pt_shift, 0), p.max_pages - 1);
+      page[tt] = p.block_table[(int64_t)sq * p.max_pages + pg];
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const bool ok = row0 + tt * 32 + col < p.n_tokens && seq[tt] >= 0 && seq[tt] < p.batch && u[tt] >= 0 &&
+                      (u[tt] >> p.pt_shift) < p.max_pages && page[tt] >= 0 && page[tt] < p.num_pages;
+      const int w = u[tt] & pt_mask;
+      slot[tt] = ok ? (int64_t)page[tt] * p.page_bytes + (int64_t)p.kind * p.kind_bytes + (w >> 2) * (NG >> 2) * 16 +
+                          (w & 3) * 4
+                    : (int64_t)-1;
+    }
+  }
+
+  // code tiles are fetched with buffer loads: a plain load before a loop and one in it would
+  // be merged into a single load at the loop head, which undoes the prefetch
+  auto cb_rsrc_of = [&](int gq) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(cb_h + (int64_t)gq * kCodes * E), (short)0, kCodes * E * 2,
+                                             kRawBufferWord3);
+  };
+  auto nrm_rsrc_of = [&](int gq) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(nrm_h + gq * kCodes), (short)0, kCodes * 4, kRawBufferWord3);
+  };
+  // A operand rows ct*32 + col of a code tile (elements [16m + 8*half, +8)) and the squared
+  // norm of codeword ct*32 + col
+  auto fetch_code = [&](__amdgpu_buffer_rsrc_t cr, __amdgpu_buffer_rsrc_t nr, int ct, u32x4* a, float& nv) {
+#pragma unroll
+    for (int m = 0; m < NMF; ++m)
+      a[m] = __builtin_amdgcn_raw_buffer_load_b128(cr, ((ct * 32 + col) * E + 16 * m + 8 * half) * 2, 0, 0);
+    nv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(nr, (ct * 32 + col) * 4, 0, 0));
+  };
+  // A operand of the norm MFMA: [-|C|^2/2 in three parts, 1, 1, 1, 0, 0] in half 0, zero in half 1
+  auto norm_operand = [&](float nv) -> u32x4 {
+    uint32_t nh, nm, nl;
+    split3(-0.5f * nv, nh, nm, nl);
+    return half == 0 ? u32x4{nh | (nm << 16), nl | (0x3f80u << 16), one2, 0u} : u32x4{0u, 0u, 0u, 0u};
+  };
+  // raw sub-vector elements [16m + 8*half, +8) of each tile's row col for group gq (direct
+  // loads read the last row for rows past the end; such rows are zeroed where used)
+  auto fetch_rows = [&](int gq, u32x4 (&xr)[TT][NMF]) {
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      if constexpr (STAGE) {
+        const int r = tt * 32 + col;
+        const int gl = gq % (kStageCh / C);   // group within the staged channels
+#pragma unroll
+        for (int m = 0; m < NMF; ++m) {
+          uint2 lo, hi;
+          if constexpr (C == 4) {             // loop steps 2*half, 2*half+1; slot gl
+            lo = *reinterpret_cast<const uint2*>(stage + stage_off<ROWS>(r, 2 * half, gl));
+            hi = *reinterpret_cast<const uint2*>(stage + stage_off<ROWS>(r, 2 * half + 1, gl));
+          } else {                            // loop step 2m + half; slots 2gl, 2gl+1
+            lo = *reinterpret_cast<const uint2*>(stage + stage_off<ROWS>(r, 2 * m + half, 2 * gl));
+            hi = *reinterpret_cast<const uint2*>(stage + stage_off<ROWS>(r, 2 * m + half, 2 * gl + 1));
+          }
+          xr[tt][m] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+      } else {
+        const int r = min(row0 + tt * 32 + col, p.n_tokens - 1);
+        const uint16_t* base = p.src + (int64_t)r * p.stride_token + (int64_t)h * p.stride_head;
+#pragma unroll
+        for (int m = 0; m < NMF; ++m) {
+          if constexpr (C == 4) {
+            const int t0 = 2 * half;      // elements 8*half .. +7 = loop steps 2*half, 2*half+1
+            const uint2 lo = *reinterpret_cast<const uint2*>(base + t0 * p.stride_loop + gq * 4);
+            const uint2 hi = *reinterpret_cast<const uint2*>(base + (t0 + 1) * p.stride_loop + gq * 4);
+            xr[tt][m] = u32x4{lo.x, lo.y, hi.x, hi.y};
+          } else {
+            const int t0 = 2 * m + half;  // elements 16m + 8*half .. +7 = loop step 2m + half
+            xr[tt][m] = *reinterpret_cast<const u32x4*>(base + t0 * p.stride_loop + gq * 8);
+          }
+        }
+      }
+    }
+  };
+  // Fill the stage with channels [ch0, ch0 + 64) with LDS-direct dword loads: wave w copies
+  // loop step w; one instruction fills 256 consecutive stage bytes (two rows, two whole
+  // 128-byte source lines), each lane fetching the source dword its stage position holds.
+  // Rows past the end read the last row.
+  auto stage_rows = [&](int ch0) {
+    const int sl = (lane >> 1) & 15;   // stage slot of this lane
+    const uint16_t* plane = p.src + (int64_t)wave * p.stride_loop + (int64_t)h * p.stride_head + ch0;
+    if (row0 + ROWS <= p.n_tokens && p.stride_token < (int64_t)1 << 30) {
+      // whole block: a uniform row-pair base plus a 32-bit lane offset
+      const uint32_t lane_off = (uint32_t)half * (uint32_t)p.stride_token * 2u + (lane & 1) * 4;
+#pragma unroll 16
+      for (int j = 0; j < ROWS / 2; ++j) {
+        const char* rows = reinterpret_cast<const char*>(plane + (int64_t)(row0 + 2 * j) * p.stride_token);
+        const uint32_t off = ((uint32_t)(sl << 3) ^ (uint32_t)((j & 15) << 3)) + lane_off;
+        __builtin_amdgcn_global_load_lds((global_void*)(rows + off), (lds_void*)(stage + (wave * ROWS + 2 * j) * 128),
+                                         4, 0, 0);
+      }
+    } else {
+      const uint16_t* src_l = plane + (lane & 1) * 2;
+#pragma unroll 4
+      for (int j = 0; j < ROWS / 2; ++j) {
+        const int row = min(row0 + 2 * j + half, p.n_tokens - 1);
+        const uint16_t* src = src_l + (int64_t)row * p.stride_token + ((sl ^ (j & 15)) << 2);
+        __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)(stage + (wave * ROWS + 2 * j) * 128), 4, 0,
+                                         0);
+      }
+    }
+  };
+  // four of the group's 256 squared codeword norms per lane (their maximum bounds the screen error)
+  auto fetch_cnorms = [&](int gq, float (&cn)[4]) {
+    const float* nrm_g = nrm_h + gq * kCodes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cn[i] = nrm_g[lane + 64 * i];
+  };
+
+  const int gend = min(g0 + groups_per_wg, NG);
+  int g = g0 + wave;
+  if (g >= gend) return;  // (a bulk workgroup owns all groups: every wave stays for the barriers)
+  u32x4 a_first[NMF];      // first code tile of the group about to be screened
+  float n_first;
+  fetch_code(cb_rsrc_of(g), nrm_rsrc_of(g), 0, a_first, n_first);
+
+  for (; g < gend; g += 4) {
+    const uint16_t* cb_g = cb_h + (int64_t)g * kCodes * E;
+    const __amdgpu_buffer_rsrc_t cb_rsrc = cb_rsrc_of(g);
+    const __amdgpu_buffer_rsrc_t nrm_rsrc = nrm_rsrc_of(g);
+    if constexpr (STAGE) {
+      if (g % (kStageCh / C) < 4) {   // first group of a staged channel range
+        __syncthreads();              // every wave is done with the previous range
+        stage_rows((g - g % (kStageCh / C)) * C);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    }
+
+    // ---- operands of this group's rows ----
+    u32x4 xb[TT][NMF];             // x, the B operand of the code MFMAs
+    u32x4 bn[TT];                  // B operand of the norm MFMA: [1, 1, 1, -|x|^2/2 in three parts, 0, 0]
+    float xn[TT];                  // |x|^2
+    float cn[4];
+    fetch_rows(g, xb);
+    fetch_cnorms(g, cn);
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const bool ok = row0 + tt * 32 + col < p.n_tokens;
       float nn = 0.f;
 #pragma unroll
       for (int m = 0; m < NMF; ++m) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (ok) {
-          if constexpr (C == 4) {
-            const int t0 = 2 * half;      // elements 8*half .. +7 = loop steps 2*half, 2*half+1
-            const uint2 lo = *reinterpret_cast<const uint2*>(base + t0 * p.stride_loop + g * 4);
-            const uint2 hi = *reinterpret_cast<const uint2*>(base + (t0 + 1) * p.stride_loop + g * 4);
-            v = u32x4{lo.x, lo.y, hi.x, hi.y};
-          } else {
-            const int t0 = 2 * m + half;  // elements 16m + 8*half .. +7 = loop step 2m + half
-            v = *reinterpret_cast<const u32x4*>(base + t0 * p.stride_loop + g * 8);
-          }
-        }
-        xb[tt][m] = u32x4{neg2_bf16x2(v[0]), neg2_bf16x2(v[1]), neg2_bf16x2(v[2]), neg2_bf16x2(v[3])};
+        if (!ok) xb[tt][m] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const float a = bf16_lo(v[w]), b = bf16_hi(v[w]);
+          const float a = bf16_lo(xb[tt][m][w]), b = bf16_hi(xb[tt][m][w]);
           nn = fmaf(a, a, nn);
           nn = fmaf(b, b, nn);
         }
@@ -115,67 +272,95 @@ __global__ void __launch_bounds__(256) encode_kernel(EncodeParams p, int groups_
       nn += __shfl_xor(nn, 32, 64);
       xn[tt] = nn;
       uint32_t xh, xm, xl;
-      split3(nn, xh, xm, xl);
+      split3(-0.5f * nn, xh, xm, xl);
       bn[tt] = half == 0 ? u32x4{one2, 0x3f80u | (xh << 16), xm | (xl << 16), 0u} : u32x4{0u, 0u, 0u, 0u};
     }
-
     // largest squared codeword norm of this group (for the screen's error bound)
-    float cmax = fmaxf(fmaxf(nrm_g[lane], nrm_g[lane + 64]), fmaxf(nrm_g[lane + 128], nrm_g[lane + 192]));
-    cmax = wave_max(cmax);
+    const float cmax = wave_max(fmaxf(fmaxf(cn[0], cn[1]), fmaxf(cn[2], cn[3])));
 
-    auto load_code = [&](int ct, u32x4* a, u32x4& an) {
-#pragma unroll
-      for (int m = 0; m < NMF; ++m)
-        a[m] = *reinterpret_cast<const u32x4*>(cb_g + (ct * 32 + col) * E + 16 * m + 8 * half);
-      uint32_t nh, nm, nl;
-      split3(nrm_g[ct * 32 + col], nh, nm, nl);
-      an = half == 0 ? u32x4{nh | (nm << 16), nl | (0x3f80u << 16), one2, 0u} : u32x4{0u, 0u, 0u, 0u};
-    };
-    auto screen = [&](const u32x4* a, const u32x4& an, int tt) -> f32x16 {
+    auto screen = [&](const u32x4* a, const u32x4& an, const u32x4* xs, const u32x4& bs) -> f32x16 {
       f32x16 acc = {};
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(an), as_bf16x8(bn[tt]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(an), as_bf16x8(bs), acc, 0, 0, 0);
 #pragma unroll
       for (int m = 0; m < NMF; ++m)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[m]), as_bf16x8(xb[tt][m]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[m]), as_bf16x8(xs[m]), acc, 0, 0, 0);
       return acc;
     };
 
-    // ---- screen: 8 tiles of 32 codewords; keep the two smallest packed keys per lane ----
-    // key = distance bits with the low 8 mantissa bits replaced by the index within the
-    // lane's codeword set (k = local + 4 * half)
+    // ---- screen: 8 tiles of 32 codewords; keep the two largest packed keys per lane ----
+    // key = F bits with the low 8 mantissa bits replaced by the index within the lane's
+    // codeword set (k = local + 4 * half).  F is at most 0 up to rounding, so a larger key
+    // holds a smaller distance and, on equal F, a smaller index.  Keys are taken two at a
+    // time: the new maximum is max3(b1, k0, k1) and the new second maximum is
+    // max(b2, med3(b1, k0, k1)) (if b2 stays among the two largest, b1 is the largest and
+    // both keys are <= b2; otherwise the two largest are among b1, k0, k1 and med3 is the
+    // smaller of them).  Keys are finite and never NaN, so no canonicalisation is needed.
     float b1[TT], b2[TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
-      b1[tt] = INFINITY;
-      b2[tt] = INFINITY;
+      b1[tt] = -INFINITY;
+      b2[tt] = -INFINITY;
     }
-    u32x4 a_cur[NMF], an_cur;
-    load_code(0, a_cur, an_cur);
-#pragma unroll 1
-    for (int ct = 0; ct < kCodes / 32; ++ct) {
-      u32x4 a_nxt[NMF], an_nxt;
-      load_code(ct + 1 < kCodes / 32 ? ct + 1 : ct, a_nxt, an_nxt);
+    // the key mask in a register (as a literal it would split each pack into two ops)
+    uint32_t keep;
+    asm("v_mov_b32 %0, %1" : "=v"(keep) : "s"(0xffffff00u));
+    auto consume = [&](const f32x16 (&acc)[TT], int ct) {
+      // first index of the tile, hidden from the optimiser: with known low bits it would
+      // split each pack into an and plus an add
+      uint32_t ctb;
+      asm("s_mov_b32 %0, %1" : "=s"(ctb) : "s"(ct * 32));
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
-        const f32x16 acc = screen(a_cur, an_cur, tt);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t kl = (uint32_t)(ct * 32 + 8 * (r >> 2) + (r & 3));
-          const float key = __uint_as_float((__float_as_uint(acc[r]) & 0xffffff00u) | kl);
-          const float ob1 = b1[tt];
-          b1[tt] = fminf(ob1, key);
-          b2[tt] = __builtin_amdgcn_fmed3f(ob1, b2[tt], key);
+        for (int r = 0; r < 16; r += 2) {
+          // index of register r in this lane's codeword set
+          const uint32_t kl = ctb + 8 * (r >> 2) + (r & 3);
+          const float k0 = __uint_as_float((__float_as_uint(acc[tt][r]) & keep) | kl);
+          const float k1 = __uint_as_float((__float_as_uint(acc[tt][r + 1]) & keep) | (kl + 1));
+          // (plain VALU operands only: the MFMA results are read by the compiled pack above,
+          // whose wait states the compiler inserts)
+          float t;
+          asm("v_med3_f32 %2, %0, %3, %4\n\t"
+              "v_max3_f32 %0, %0, %3, %4\n\t"
+              "v_max_f32 %1, %1, %2"
+              : "+v"(b1[tt]), "+v"(b2[tt]), "=&v"(t)
+              : "v"(k0), "v"(k1));
         }
       }
+    };
+    u32x4 a_cur[NMF];
+    float n_cur = n_first;
+#pragma unroll
+    for (int m = 0; m < NMF; ++m) a_cur[m] = a_first[m];
+#pragma unroll 1
+    for (int ct = 0; ct < kCodes / 32 - 1; ++ct) {
+      u32x4 a_nxt[NMF];
+      float n_nxt;
+      fetch_code(cb_rsrc, nrm_rsrc, ct + 1, a_nxt, n_nxt);
+      const u32x4 an_cur = norm_operand(n_cur);
+      f32x16 acc[TT];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) acc[tt] = screen(a_cur, an_cur, xb[tt], bn[tt]);
+      consume(acc, ct);
 #pragma unroll
       for (int m = 0; m < NMF; ++m) a_cur[m] = a_nxt[m];
-      an_cur = an_nxt;
+      n_cur = n_nxt;
+    }
+    {
+      // last tile: its products are issued first, then the next group's first code tile is
+      // fetched so that it arrives while this group is finished
+      const u32x4 an_cur = norm_operand(n_cur);
+      f32x16 acc[TT];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) acc[tt] = screen(a_cur, an_cur, xb[tt], bn[tt]);
+      if (g + 4 < gend) fetch_code(cb_rsrc_of(g + 4), nrm_rsrc_of(g + 4), 0, a_first, n_first);
+      consume(acc, kCodes / 32 - 1);
     }
 
     // ---- merge the two half-waves and decide ----
     uint32_t best[TT];
     bool rerank[TT];
-    float thr[TT];
+    float fthr[TT];   // re-rank candidates have F >= fthr
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       const bool ok = row0 + tt * 32 + col < p.n_tokens;
@@ -184,24 +369,24 @@ __global__ void __launch_bounds__(256) encode_kernel(EncodeParams p, int groups_
       const float ob2 = __shfl_xor(b2[tt], 32, 64);
       const uint32_t myk = (__float_as_uint(b1[tt]) & 0xffu) + 4u * half;
       const uint32_t ok1 = (__float_as_uint(ob1) & 0xffu) + 4u * (half ^ 1);
-      const float v1 = __uint_as_float(__float_as_uint(b1[tt]) & 0xffffff00u);
-      const float w1 = __uint_as_float(__float_as_uint(ob1) & 0xffffff00u);
-      float nb1, nb2;
-      uint32_t nk1;
-      if (w1 < v1 || (w1 == v1 && ok1 < myk)) {
-        nb1 = w1;
-        nk1 = ok1;
-        nb2 = fminf(v1, __uint_as_float(__float_as_uint(ob2) & 0xffffff00u));
+      const float v1 = key_value(b1[tt]), w1 = key_value(ob1);
+      float f1, f2;
+      uint32_t k1;
+      if (w1 > v1 || (w1 == v1 && ok1 < myk)) {
+        f1 = w1;
+        k1 = ok1;
+        f2 = fmaxf(v1, key_value(ob2));
       } else {
-        nb1 = v1;
-        nk1 = myk;
-        nb2 = fminf(__uint_as_float(__float_as_uint(b2[tt]) & 0xffffff00u), w1);
+        f1 = v1;
+        k1 = myk;
+        f2 = fmaxf(key_value(b2[tt]), w1);
       }
+      const float d1 = -2.f * f1, d2 = -2.f * f2;                            // screened distances
       const float delta = 1.52587890625e-05f * (xn[tt] + cmax);              // 2^-16 (|x|^2 + max|C|^2)
-      const float trunc = 6.103515625e-05f * fmaxf(fabsf(nb1), fabsf(nb2));   // 2^-14 max(|b1|, |b2|)
-      rerank[tt] = ok && !(nb2 - nb1 > 2.f * delta + trunc);
-      thr[tt] = nb1 + 6.103515625e-05f * fabsf(nb1) + 2.f * delta + trunc;
-      best[tt] = nk1;
+      const float trunc = 6.103515625e-05f * fmaxf(fabsf(d1), fabsf(d2));    // 2^-14 max(|d1|, |d2|)
+      rerank[tt] = ok && !(d2 - d1 > 2.f * delta + trunc);
+      fthr[tt] = -0.5f * (d1 + 6.103515625e-05f * fabsf(d1) + 2.f * delta + trunc);
+      best[tt] = k1;
     }
 
     // ---- rare: exact re-rank.  The tile is screened again and every codeword whose screened
@@ -216,7 +401,7 @@ __global__ void __launch_bounds__(256) encode_kernel(EncodeParams p, int groups_
         // the selected tile's operands, picked with uniform selects (no dynamic register indexing)
         u32x4 xs[NMF], bs = bn[0];
         bool rs = rerank[0];
-        float ts_thr = thr[0];
+        float ts_thr = fthr[0];
 #pragma unroll
         for (int m = 0; m < NMF; ++m) xs[m] = xb[0][m];
 #pragma unroll
@@ -226,39 +411,30 @@ __global__ void __launch_bounds__(256) encode_kernel(EncodeParams p, int groups_
             for (int m = 0; m < NMF; ++m) xs[m] = xb[tt][m];
             bs = bn[tt];
             rs = rerank[tt];
-            ts_thr = thr[tt];
+            ts_thr = fthr[tt];
           }
         }
         if (!__any(rs)) continue;
-        // park the rows (x = -0.5 * (-2x), exact) in LDS for the fp64 pass
+        // park the rows in LDS for the fp64 pass
 #pragma unroll
-        for (int m = 0; m < NMF; ++m) {
-          u32x4 xw;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const uint32_t nw = xs[m][w];
-            const float lo = -0.5f * bf16_lo(nw), hi = -0.5f * bf16_hi(nw);
-            xw[w] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
-          }
-          xrow[wave][col][2 * m + half] = xw;
-        }
+        for (int m = 0; m < NMF; ++m) xrow[wave][col][2 * m + half] = xs[m];
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         double bd = INFINITY;
         uint32_t bk = 0xffffffffu;
+        u32x4 ra[NMF];
+        float rn;
+        fetch_code(cb_rsrc, nrm_rsrc, 0, ra, rn);
 #pragma unroll 1
         for (int ct = 0; ct < kCodes / 32; ++ct) {
-          u32x4 a[NMF], an;
-          load_code(ct, a, an);
-          f32x16 acc = {};
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(an), as_bf16x8(bs), acc, 0, 0, 0);
-#pragma unroll
-          for (int m = 0; m < NMF; ++m)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[m]), as_bf16x8(xs[m]), acc, 0, 0, 0);
+          u32x4 ra_nxt[NMF];
+          float rn_nxt;
+          fetch_code(cb_rsrc, nrm_rsrc, ct + 1 < kCodes / 32 ? ct + 1 : ct, ra_nxt, rn_nxt);
+          const f32x16 acc = screen(ra, norm_operand(rn), xs, bs);
           uint32_t mask = 0u;
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) mask |= (acc[rr] <= ts_thr ? 1u : 0u) << rr;
+          for (int rr = 0; rr < 16; ++rr) mask |= (acc[rr] >= ts_thr ? 1u : 0u) << rr;
           if (!rs) mask = 0u;
           while (mask) {                      // candidates of this lane (rare, divergent)
             const int rr = __builtin_ctz(mask);
@@ -283,6 +459,9 @@ __global__ void __launch_bounds__(256) encode_kernel(EncodeParams p, int groups_
               bk = k;
             }
           }
+#pragma unroll
+          for (int m = 0; m < NMF; ++m) ra[m] = ra_nxt[m];
+          rn = rn_nxt;
         }
         // merge the two halves' exact candidates (lowest index on equal distance)
         const double obd = __shfl_xor(bd, 32, 64);
@@ -302,17 +481,7 @@ __global__ void __launch_bounds__(256) encode_kernel(EncodeParams p, int groups_
       const int r = row0 + tt * 32 + col;
       if (half == 0 && r < p.n_tokens) {
         if (p.out_idx) p.out_idx[((int64_t)r * p.Hkv + h) * NG + g] = (int)best[tt];
-        const int seq = p.seq_id[r];
-        const int u = p.vq_pos[r];
-        if (seq >= 0 && seq < p.batch && u >= 0 && (u >> p.pt_shift) < p.max_pages) {
-          const int page = p.block_table[(int64_t)seq * p.max_pages + (u >> p.pt_shift)];
-          if (page >= 0 && page < p.num_pages) {
-            const int w = u & pt_mask;
-            const int64_t off = (int64_t)page * p.page_bytes + (int64_t)p.kind * p.kind_bytes +
-                                ((w >> 2) * (NG >> 2) + (g >> 2)) * 16 + (w & 3) * 4 + (g & 3);
-            pool_h[off] = (uint8_t)best[tt];
-          }
-        }
+        if (slot[tt] >= 0) pool_h[slot[tt] + (g >> 2) * 16 + (g & 3)] = (uint8_t)best[tt];
       }
     }
   }
@@ -328,15 +497,21 @@ hipError_t launch_encode(const EncodeParams& p, int c, hipStream_t stream) {
   const bool small = (int64_t)p.n_tokens * p.Hkv < 16384;
   const int groups_per_wg = small ? 4 : p.NG;
   const int rows_per_wg = small ? 64 : 128;
-  const dim3 grid((p.NG + groups_per_wg - 1) / groups_per_wg, (p.n_tokens + rows_per_wg - 1) / rows_per_wg, p.Hkv);
+  const int gx = (p.NG + groups_per_wg - 1) / groups_per_wg;
+  const int gy = (p.n_tokens + rows_per_wg - 1) / rows_per_wg;
+  const int64_t blocks = (int64_t)gx * gy * p.Hkv;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks);
+  // the staged bulk path takes 64 channels at a time
+  if (!small && (p.NG * c) % kStageCh != 0) return hipErrorInvalidValue;
   if (c == 4 && small)
-    hipLaunchKernelGGL((encode_kernel<4, 2>), grid, dim3(256), 0, stream, p, groups_per_wg);
+    hipLaunchKernelGGL((encode_kernel<4, 2, false>), grid, dim3(256), 0, stream, p, groups_per_wg, gx, gy);
   else if (c == 4)
-    hipLaunchKernelGGL((encode_kernel<4, 4>), grid, dim3(256), 0, stream, p, groups_per_wg);
+    hipLaunchKernelGGL((encode_kernel<4, 4, true>), grid, dim3(256), 0, stream, p, groups_per_wg, gx, gy);
   else if (c == 8 && small)
-    hipLaunchKernelGGL((encode_kernel<8, 2>), grid, dim3(256), 0, stream, p, groups_per_wg);
+    hipLaunchKernelGGL((encode_kernel<8, 2, false>), grid, dim3(256), 0, stream, p, groups_per_wg, gx, gy);
   else if (c == 8)
-    hipLaunchKernelGGL((encode_kernel<8, 4>), grid, dim3(256), 0, stream, p, groups_per_wg);
+    hipLaunchKernelGGL((encode_kernel<8, 4, true>), grid, dim3(256), 0, stream, p, groups_per_wg, gx, gy);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
