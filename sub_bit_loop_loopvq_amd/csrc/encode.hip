@@ -24,9 +24,9 @@
 //  * exactness: the screen errs by at most delta = 2^-16 (||x||^2 + max_k ||C_k||^2) in
 //    distance and the packing truncates by at most 2^-15 relative.  If the two smallest
 //    distances are further apart than both bounds allow, the screened winner is the
-//    exact argmin.  Otherwise the row's tile is screened again and every codeword within
-//    the bound of the minimum is re-scored as a sequential fp64 sum of squared
-//    differences; the lowest exact minimiser wins (the brute-force definition).
+//    exact argmin.  Otherwise (about one row in a thousand) the whole wave scores that row
+//    against all 256 codewords as sequential fp64 sums of squared differences and keeps
+//    the lowest exact minimiser (the brute-force definition).
 //  * packing: the 8-bit index is stored as one byte of its 16-index micro-tile
 //    (token quad x group quad) in the page the block table maps its position to.
 #include "lvq_common.h"
@@ -99,7 +99,6 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
   uint8_t* pool_h = p.pool_lj + (int64_t)h * p.head_stride;
   const int pt_mask = (1 << p.pt_shift) - 1;
   const uint32_t one2 = 0x3f803f80u;   // two bf16 ones
-  __shared__ u32x4 xrow[4][32][E / 8];  // exact re-rank: the 32 sub-vectors of one tile per wave
   __shared__ __align__(16) uint8_t stage[STAGE ? 4 * ROWS * 128 : 16];
 
   // byte offset (within the kv-head's pool) of each row's micro-tile slot for group 0, or -1
@@ -360,7 +359,6 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
     // ---- merge the two half-waves and decide ----
     uint32_t best[TT];
     bool rerank[TT];
-    float fthr[TT];   // re-rank candidates have F >= fthr
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       const bool ok = row0 + tt * 32 + col < p.n_tokens;
@@ -385,93 +383,66 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
       const float delta = 1.52587890625e-05f * (xn[tt] + cmax);              // 2^-16 (|x|^2 + max|C|^2)
       const float trunc = 6.103515625e-05f * fmaxf(fabsf(d1), fabsf(d2));    // 2^-14 max(|d1|, |d2|)
       rerank[tt] = ok && !(d2 - d1 > 2.f * delta + trunc);
-      fthr[tt] = -0.5f * (d1 + 6.103515625e-05f * fabsf(d1) + 2.f * delta + trunc);
       best[tt] = k1;
     }
 
-    // ---- rare: exact re-rank.  The tile is screened again and every codeword whose screened
-    //      distance is within the bound of the minimum is re-scored in fp64 (sequential over
-    //      elements, no fused operations); the lowest exact minimiser wins. ----
+    // ---- rare: exact re-rank of the rows whose screen is not conclusive.  For each such row
+    //      the whole wave scores all 256 codewords exactly, 4 per lane, as fp64 sums of squared
+    //      differences taken in element order with no fused operations (the brute-force
+    //      definition), and takes the lowest index among the minimisers. ----
     bool any_rr = false;
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) any_rr |= rerank[tt];
     if (__any(any_rr)) {
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        uint64_t rows = __ballot(rerank[tt] && half == 0);
+        while (rows) {
+          const int rc = __builtin_ctzll(rows);   // the row's column in the tile (uniform)
+          rows &= rows - 1;
+          // the row's elements, two per word: word e2 holds elements 2*e2, 2*e2 + 1 and sits
+          // in word e2 % 4 of B operand e2 / 8, half (e2 / 4) % 2
+          uint32_t xw[E / 2];
+#pragma unroll
+          for (int e2 = 0; e2 < E / 2; ++e2)
+            xw[e2] = (uint32_t)__builtin_amdgcn_readlane((int)xb[tt][e2 >> 3][e2 & 3], rc + 32 * ((e2 >> 2) & 1));
+          double bd = INFINITY;
+          uint32_t bk = 0u;
 #pragma unroll 1
-      for (int ts = 0; ts < TT; ++ts) {
-        // the selected tile's operands, picked with uniform selects (no dynamic register indexing)
-        u32x4 xs[NMF], bs = bn[0];
-        bool rs = rerank[0];
-        float ts_thr = fthr[0];
-#pragma unroll
-        for (int m = 0; m < NMF; ++m) xs[m] = xb[0][m];
-#pragma unroll
-        for (int tt = 1; tt < TT; ++tt) {
-          if (ts == tt) {
-#pragma unroll
-            for (int m = 0; m < NMF; ++m) xs[m] = xb[tt][m];
-            bs = bn[tt];
-            rs = rerank[tt];
-            ts_thr = fthr[tt];
-          }
-        }
-        if (!__any(rs)) continue;
-        // park the rows in LDS for the fp64 pass
-#pragma unroll
-        for (int m = 0; m < NMF; ++m) xrow[wave][col][2 * m + half] = xs[m];
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        double bd = INFINITY;
-        uint32_t bk = 0xffffffffu;
-        u32x4 ra[NMF];
-        float rn;
-        fetch_code(cb_rsrc, nrm_rsrc, 0, ra, rn);
-#pragma unroll 1
-        for (int ct = 0; ct < kCodes / 32; ++ct) {
-          u32x4 ra_nxt[NMF];
-          float rn_nxt;
-          fetch_code(cb_rsrc, nrm_rsrc, ct + 1 < kCodes / 32 ? ct + 1 : ct, ra_nxt, rn_nxt);
-          const f32x16 acc = screen(ra, norm_operand(rn), xs, bs);
-          uint32_t mask = 0u;
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) mask |= (acc[rr] >= ts_thr ? 1u : 0u) << rr;
-          if (!rs) mask = 0u;
-          while (mask) {                      // candidates of this lane (rare, divergent)
-            const int rr = __builtin_ctz(mask);
-            mask &= mask - 1u;
-            const uint32_t k = (uint32_t)(ct * 32 + 8 * (rr >> 2) + 4 * half + (rr & 3));
+          for (int i = 0; i < kCodes / 64; ++i) {
+            const uint32_t k = (uint32_t)(lane + 64 * i);
             const u32x4* ck = reinterpret_cast<const u32x4*>(cb_g + k * E);
             double dd = 0.0;
-#pragma unroll 1
+#pragma unroll
             for (int e8 = 0; e8 < E / 8; ++e8) {
-              const u32x4 xv = xrow[wave][col][e8];
               const u32x4 cv = ck[e8];
 #pragma unroll
               for (int w = 0; w < 4; ++w) {
-                const double d0 = __dsub_rn((double)bf16_lo(xv[w]), (double)bf16_lo(cv[w]));
+                const uint32_t xv = xw[4 * e8 + w];
+                const double d0 = __dsub_rn((double)bf16_lo(xv), (double)bf16_lo(cv[w]));
                 dd = __dadd_rn(dd, __dmul_rn(d0, d0));
-                const double d1 = __dsub_rn((double)bf16_hi(xv[w]), (double)bf16_hi(cv[w]));
+                const double d1 = __dsub_rn((double)bf16_hi(xv), (double)bf16_hi(cv[w]));
                 dd = __dadd_rn(dd, __dmul_rn(d1, d1));
               }
             }
-            if (dd < bd || (dd == bd && k < bk)) {
+            if (dd < bd) {   // k grows with i: a strict comparison keeps the lowest index
               bd = dd;
               bk = k;
             }
           }
+          // wave minimum of (distance, index)
 #pragma unroll
-          for (int m = 0; m < NMF; ++m) ra[m] = ra_nxt[m];
-          rn = rn_nxt;
+          for (int off = 32; off >= 1; off >>= 1) {
+            const double od = __shfl_xor(bd, off, 64);
+            const uint32_t ok2 = __shfl_xor(bk, off, 64);
+            if (od < bd || (od == bd && ok2 < bk)) {
+              bd = od;
+              bk = ok2;
+            }
+          }
+          if (col == rc) best[tt] = bk;
+          if (p.rerank_count && lane == 0) atomicAdd(p.rerank_count, 1ull);
         }
-        // merge the two halves' exact candidates (lowest index on equal distance)
-        const double obd = __shfl_xor(bd, 32, 64);
-        const uint32_t obk = __shfl_xor(bk, 32, 64);
-        if (obd < bd || (obd == bd && obk < bk)) bk = obk;
-        if (rs && p.rerank_count && half == 0) atomicAdd(p.rerank_count, 1ull);
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-          if (ts == tt && rs) best[tt] = bk;
-        __builtin_amdgcn_wave_barrier();
       }
     }
 
