@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "VQ decode-attn queries/s + effective HBM GB/s (% peak), 32K ctx, 0.5 bit/elem"
 HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "stack24x4_h16_d128_b64_n32k"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stack32k_traffic.md")
 DECODE_SRC = os.path.join(ROOT, "sub_bit_loop_loopvq_amd", "csrc", "decode_attn.hip")
 
@@ -223,6 +224,141 @@ def cpu_baseline(wl, seconds: float) -> dict:
                        f"(wall {time.time() - t_start:.1f}s)")}
 
 
+ENCODE_METRIC = "LoopVQ bulk encode sub-vectors/s (one layer, loop group and kind)"
+# VALU lane-operations per second of one MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+VALU_PEAK_OPS = 256 * 4 * 16 * 2.4e9
+
+
+class EncodeBench:
+    """Bulk encode of one (layer, loop group, kind) slice: all rows, kv-heads and groups in one call."""
+
+    def __init__(self, wl, layer=0, loop_group=0, kind=0, seed=0):
+        import torch
+        import sub_bit_loop_loopvq_amd as lvq
+        from synth import gen
+        from synth.device import DeviceGen
+        self.torch, self.lvq, self.wl = torch, lvq, wl
+        self.layer, self.j, self.kind = layer, loop_group, kind
+        dev = "cuda"
+        B, H, d, G, P = wl.batch, wl.kv_heads, wl.head_dim, wl.loop_group, wl.prefix
+        self.rows = rows = wl.encode_tokens
+        per_seq = rows // B
+        self.cfg = lvq.make_config(wl)
+        self.pps = -(-per_seq // wl.page_tokens)
+        self.num_pages = B * self.pps
+        self.lay = lvq.loopvq_layout_query(self.cfg, B, self.num_pages)
+        perm = np.random.default_rng(seed).permutation(self.num_pages).astype(np.int32)
+        self.bt = torch.from_numpy(perm.reshape(B, self.pps)).to(dev)
+        sc = gen.scales(wl)
+        cb = gen.codebooks(wl, kind, sc, layers=[layer])
+        self.cb = torch.from_numpy(cb.view(np.int16)).to(dev)
+        self.norms = torch.empty(self.lay.norms_elems, dtype=torch.float32, device=dev)
+        lvq.loopvq_codebook_prepare(self.cfg, self.cb, torch.empty_like(self.cb), self.norms)
+        self.src = torch.empty((G, rows, H, d), dtype=torch.int16, device=dev)
+        dg = DeviceGen(wl)
+        for b in range(B):
+            dg.kv(self.src[:, b * per_seq:], kind=kind, layer=layer, b0=b, nb=1, h0=0, nh=H, n0=P, nn=per_seq,
+                  t0=loop_group * G, nt=G, s_loop=rows * H * d, s_b=0, s_h=d, s_n=H * d)
+        r = torch.arange(rows, dtype=torch.int32, device=dev)
+        self.seq, self.pos = r // per_seq, r % per_seq
+        # the pool slice of this (layer, loop group); the library addresses it from the pool base
+        slice_bytes = H * self.lay.pool_head_stride_bytes
+        self.pool = torch.zeros(slice_bytes, dtype=torch.uint8, device=dev)
+        self.shift = (layer * wl.loop_groups + loop_group) * slice_bytes
+        self.rerank = torch.zeros(1, dtype=torch.int64, device=dev)
+        torch.cuda.synchronize()
+
+    def run(self, count=None):
+        wl = self.wl
+        self.lvq.loopvq_encode(self.cfg, layer=self.layer, loop_group=self.j, kind=self.kind, n_tokens=self.rows,
+                               src=self.src, stride_loop=self.rows * wl.kv_heads * wl.head_dim,
+                               stride_token=wl.kv_heads * wl.head_dim, stride_head=wl.head_dim, seq_id=self.seq,
+                               vq_pos=self.pos, block_table=self.bt, batch=wl.batch, max_pages_per_seq=self.pps,
+                               num_pages=self.num_pages, cb=self.cb, cb_norms=self.norms,
+                               pool=self.pool.data_ptr() - self.shift, rerank_count=count)
+
+
+def encode_cpu_baseline(wl, seconds: float, layer=0, loop_group=0, kind=0) -> dict:
+    """The CPU oracle's brute-force encode (fp64, single BLAS thread) on sampled sub-vectors of the slice."""
+    from threadpoolctl import threadpool_limits
+    from oracle import loopvq_oracle as O
+    from synth import gen
+    t_start = time.time()
+    sc = gen.scales(wl)
+    cb = gen.bf16_to_f64(gen.codebooks(wl, kind, sc, layers=[layer])[layer, 0])   # [H][NG][K][E]
+    per_seq = wl.encode_tokens // wl.batch
+    G = wl.loop_group
+    done, busy, rows = 0, 0.0, 0
+    with threadpool_limits(limits=1):
+        for h in range(wl.kv_heads):
+            planes = gen.kv_tokens(wl, kind, layer, 0, h, wl.prefix, wl.prefix + per_seq, loop_group * G,
+                                   loop_group * G + G, sc)                                  # [n][G][d]
+            x = O.subvectors(gen.bf16_to_f64(planes).transpose(1, 0, 2), wl.chans)            # [n][NG][E]
+            for n0 in range(0, per_seq, 256):
+                c0 = time.perf_counter()
+                for g in range(wl.groups):
+                    O.encode(x[n0:n0 + 256, g], cb[h, g])
+                busy += time.perf_counter() - c0
+                done += 256 * wl.groups
+                rows += 256
+                if busy >= seconds:
+                    break
+            if busy >= seconds:
+                break
+    return {"value": done / busy, "unit": "sub-vectors/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{done} sub-vectors ({rows} (token, kv-head) rows of sequence 0 x {wl.groups} groups) of "
+                       f"layer {layer}, loop group {loop_group}, kind {kind}: brute-force fp64 distances to all "
+                       f"{wl.codewords} codewords + argmin; {busy:.1f}s of timed oracle work, 1 BLAS thread; input "
+                       f"setup untimed (wall {time.time() - t_start:.1f}s)")}
+
+
+def encode_main(args):
+    import torch
+    from synth import workloads as W
+    wl = W.BY_NAME[args.workload]
+    torch.cuda.set_device(0)
+    eb = EncodeBench(wl)
+    for _ in range(args.warmup):
+        eb.run()
+    eb.rerank.zero_()
+    events = []
+    E = torch.cuda.Event
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        e0, e1 = E(enable_timing=True), E(enable_timing=True)
+        e0.record()
+        eb.run(eb.rerank)
+        e1.record()
+        events.append((e0, e1))
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in events])
+    avg = float(us.mean())
+    subvec = wl.encode_tokens * wl.kv_heads * wl.groups
+    in_bytes = subvec * wl.sub_len * 2
+    out_bytes = subvec * wl.index_bits // 8
+    compares = subvec * wl.codewords
+    rec = {
+        "metric": ENCODE_METRIC, "value": subvec / (avg * 1e-6), "unit": "sub-vectors/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": avg * 1e-3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": wl.encode_tokens, "kv_heads": wl.kv_heads, "groups": wl.groups,
+                   "sub_len": wl.sub_len, "codewords": wl.codewords, "layer": 0, "loop_group": 0, "kind": "K"},
+        "tokens_per_s": wl.encode_tokens / (avg * 1e-6),
+        "roofline": {"bound": "hbm", "achieved": (in_bytes + out_bytes) / (avg * 1e-6) / 1e9,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": (in_bytes + out_bytes) / (avg * 1e-6) / 1e9 / HBM_PEAK_GBPS, "traffic": None},
+        "valu_roofline": {"bound": "alu", "achieved": compares / (avg * 1e-6) / 1e12,
+                          "peak": VALU_PEAK_OPS / 1e12, "unit": "Tcompare/s at one VALU op per compare",
+                          "frac": compares / (avg * 1e-6) / VALU_PEAK_OPS},
+        "launch_us": {"mean": avg, "p10": float(np.percentile(us, 10)), "p50": float(np.percentile(us, 50)),
+                      "p90": float(np.percentile(us, 90))},
+        "reranked_fraction": int(eb.rerank.item()) / (subvec * args.steps),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = encode_cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
 def copy_calibration(nbytes: int, reps: int) -> None:
     """A plain device copy of known size, for scaling HBM counters (rocprofv3 --pmc)."""
     import torch
@@ -240,16 +376,24 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="stack24x4_h16_d128_b64_n32k")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, help="bytes; run only a plain copy (counter scaling)")
+    ap.add_argument("--encode", action="store_true",
+                    help="time the bulk encode of one (layer, loop group, kind) slice instead of the decode step "
+                         "(default workload for this mode: deep4x32_h32_d128_b16_n8k)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 5)
+        return
+    if args.encode:
+        if args.workload == DEFAULT_WORKLOAD:
+            args.workload = "deep4x32_h32_d128_b16_n8k"
+        encode_main(args)
         return
     import torch
     from synth import workloads as W

@@ -68,6 +68,9 @@ __device__ __forceinline__ int xcd_local_block(int L, int n) {
   return x * per + (x < rem ? x : rem) + (L >> 3);
 }
 
+// channel groups per kv-head the kernels take (d / c <= 32)
+constexpr int kMaxGroups = 32;
+
 // Bulk stage: channels [ch0, ch0 + 64) of the block's rows for the 4 loop steps, as
 // [loop step t][row r][64 channels] bf16 (128 B per row).  The 8-byte slot s (4 channels) of
 // row r sits at slot s ^ ((r >> 1) & 15) of its row, so the 32 rows that a half-wave reads at
@@ -100,11 +103,25 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
   const int pt_mask = (1 << p.pt_shift) - 1;
   const uint32_t one2 = 0x3f803f80u;   // two bf16 ones
   __shared__ __align__(16) uint8_t stage[STAGE ? 4 * ROWS * 128 : 16];
+  // rows whose screen is not conclusive, as (row in block) * 32 + group, re-ranked exactly
+  // after the screen so that no wave holds up the others in the middle of it
+  __shared__ uint16_t rr_list[ROWS * kMaxGroups];
+  __shared__ int rr_n;
+  if (threadIdx.x == 0) rr_n = 0;
+  __syncthreads();
 
   // byte offset (within the kv-head's pool) of each row's micro-tile slot for group 0, or -1
   // when the row is past the end, its sequence or position is out of range or its page is
   // unmapped; group g adds (g / 4) * 16 + g % 4.  (All loads are issued unconditionally at
   // clamped addresses, then validated.)
+  auto slot_of = [&](int r) -> int64_t {   // the same for one row, with plain loads (re-rank)
+    const int sq = p.seq_id[r], u = p.vq_pos[r];
+    if (sq < 0 || sq >= p.batch || u < 0 || (u >> p.pt_shift) >= p.max_pages) return -1;
+    const int page = p.block_table[(int64_t)sq * p.max_pages + (u >> p.pt_shift)];
+    if (page < 0 || page >= p.num_pages) return -1;
+    const int w = u & pt_mask;
+    return (int64_t)page * p.page_bytes + (int64_t)p.kind * p.kind_bytes + (w >> 2) * (NG >> 2) * 16 + (w & 3) * 4;
+  };
   int64_t slot[TT];
   {
     int seq[TT], u[TT], page[TT];
@@ -198,10 +215,11 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
   // Rows past the end read the last row.
   auto stage_rows = [&](int ch0) {
     const int sl = (lane >> 1) & 15;   // stage slot of this lane
-    const uint16_t* plane = p.src + (int64_t)wave * p.stride_loop + (int64_t)h * p.stride_head + ch0;
+    const uint16_t* plane = p.src + (int64_t)wave * p.stride_loop + (int64_t)h * p.stride_head;
     if (row0 + ROWS <= p.n_tokens && p.stride_token < (int64_t)1 << 30) {
-      // whole block: a uniform row-pair base plus a 32-bit lane offset
-      const uint32_t lane_off = (uint32_t)half * (uint32_t)p.stride_token * 2u + (lane & 1) * 4;
+      // whole block: a uniform row-pair base plus a 32-bit lane offset (which includes the
+      // channel range, so that it is not kept live outside this function)
+      const uint32_t lane_off = (uint32_t)half * (uint32_t)p.stride_token * 2u + (lane & 1) * 4 + ch0 * 2;
 #pragma unroll 16
       for (int j = 0; j < ROWS / 2; ++j) {
         const char* rows = reinterpret_cast<const char*>(plane + (int64_t)(row0 + 2 * j) * p.stride_token);
@@ -210,7 +228,7 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
                                          4, 0, 0);
       }
     } else {
-      const uint16_t* src_l = plane + (lane & 1) * 2;
+      const uint16_t* src_l = plane + ch0 + (lane & 1) * 2;
 #pragma unroll 4
       for (int j = 0; j < ROWS / 2; ++j) {
         const int row = min(row0 + 2 * j + half, p.n_tokens - 1);
@@ -228,13 +246,12 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
   };
 
   const int gend = min(g0 + groups_per_wg, NG);
-  int g = g0 + wave;
-  if (g >= gend) return;  // (a bulk workgroup owns all groups: every wave stays for the barriers)
   u32x4 a_first[NMF];      // first code tile of the group about to be screened
   float n_first;
-  fetch_code(cb_rsrc_of(g), nrm_rsrc_of(g), 0, a_first, n_first);
+  if (g0 + wave < gend) fetch_code(cb_rsrc_of(g0 + wave), nrm_rsrc_of(g0 + wave), 0, a_first, n_first);
 
-  for (; g < gend; g += 4) {
+  // (a bulk workgroup owns all groups, so every wave passes the same staging barriers)
+  for (int g = g0 + wave; g < gend; g += 4) {
     const uint16_t* cb_g = cb_h + (int64_t)g * kCodes * E;
     const __amdgpu_buffer_rsrc_t cb_rsrc = cb_rsrc_of(g);
     const __amdgpu_buffer_rsrc_t nrm_rsrc = nrm_rsrc_of(g);
@@ -380,69 +397,18 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
         f2 = fmaxf(key_value(b2[tt]), w1);
       }
       const float d1 = -2.f * f1, d2 = -2.f * f2;                            // screened distances
-      const float delta = 1.52587890625e-05f * (xn[tt] + cmax);              // 2^-16 (|x|^2 + max|C|^2)
+      const float delta = 7.62939453125e-06f * (xn[tt] + cmax);              // 2^-17 (|x|^2 + max|C|^2)
       const float trunc = 6.103515625e-05f * fmaxf(fabsf(d1), fabsf(d2));    // 2^-14 max(|d1|, |d2|)
       rerank[tt] = ok && !(d2 - d1 > 2.f * delta + trunc);
       best[tt] = k1;
     }
 
-    // ---- rare: exact re-rank of the rows whose screen is not conclusive.  For each such row
-    //      the whole wave scores all 256 codewords exactly, 4 per lane, as fp64 sums of squared
-    //      differences taken in element order with no fused operations (the brute-force
-    //      definition), and takes the lowest index among the minimisers. ----
-    bool any_rr = false;
+    // ---- rows whose screen is not conclusive go to the exact re-rank list ----
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) any_rr |= rerank[tt];
-    if (__any(any_rr)) {
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        uint64_t rows = __ballot(rerank[tt] && half == 0);
-        while (rows) {
-          const int rc = __builtin_ctzll(rows);   // the row's column in the tile (uniform)
-          rows &= rows - 1;
-          // the row's elements, two per word: word e2 holds elements 2*e2, 2*e2 + 1 and sits
-          // in word e2 % 4 of B operand e2 / 8, half (e2 / 4) % 2
-          uint32_t xw[E / 2];
-#pragma unroll
-          for (int e2 = 0; e2 < E / 2; ++e2)
-            xw[e2] = (uint32_t)__builtin_amdgcn_readlane((int)xb[tt][e2 >> 3][e2 & 3], rc + 32 * ((e2 >> 2) & 1));
-          double bd = INFINITY;
-          uint32_t bk = 0u;
-#pragma unroll 1
-          for (int i = 0; i < kCodes / 64; ++i) {
-            const uint32_t k = (uint32_t)(lane + 64 * i);
-            const u32x4* ck = reinterpret_cast<const u32x4*>(cb_g + k * E);
-            double dd = 0.0;
-#pragma unroll
-            for (int e8 = 0; e8 < E / 8; ++e8) {
-              const u32x4 cv = ck[e8];
-#pragma unroll
-              for (int w = 0; w < 4; ++w) {
-                const uint32_t xv = xw[4 * e8 + w];
-                const double d0 = __dsub_rn((double)bf16_lo(xv), (double)bf16_lo(cv[w]));
-                dd = __dadd_rn(dd, __dmul_rn(d0, d0));
-                const double d1 = __dsub_rn((double)bf16_hi(xv), (double)bf16_hi(cv[w]));
-                dd = __dadd_rn(dd, __dmul_rn(d1, d1));
-              }
-            }
-            if (dd < bd) {   // k grows with i: a strict comparison keeps the lowest index
-              bd = dd;
-              bk = k;
-            }
-          }
-          // wave minimum of (distance, index)
-#pragma unroll
-          for (int off = 32; off >= 1; off >>= 1) {
-            const double od = __shfl_xor(bd, off, 64);
-            const uint32_t ok2 = __shfl_xor(bk, off, 64);
-            if (od < bd || (od == bd && ok2 < bk)) {
-              bd = od;
-              bk = ok2;
-            }
-          }
-          if (col == rc) best[tt] = bk;
-          if (p.rerank_count && lane == 0) atomicAdd(p.rerank_count, 1ull);
-        }
+    for (int tt = 0; tt < TT; ++tt) {
+      if (rerank[tt] && half == 0) {
+        const int e = atomicAdd(&rr_n, 1);
+        rr_list[e] = (uint16_t)(((tt * 32 + col) << 5) | g);
       }
     }
 
@@ -450,10 +416,73 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       const int r = row0 + tt * 32 + col;
-      if (half == 0 && r < p.n_tokens) {
+      if (half == 0 && r < p.n_tokens && !rerank[tt]) {
         if (p.out_idx) p.out_idx[((int64_t)r * p.Hkv + h) * NG + g] = (int)best[tt];
         if (slot[tt] >= 0) pool_h[slot[tt] + (g >> 2) * 16 + (g & 3)] = (uint8_t)best[tt];
       }
+    }
+  }
+
+  // ---- exact re-rank of the listed rows: for each, the whole wave scores all 256 codewords,
+  //      4 per lane, as fp64 sums of squared differences taken in element order with a
+  //      separate rounding of every product and sum (the brute-force definition, no fused
+  //      operations), and keeps the lowest index among the minimisers ----
+  __syncthreads();
+  const int nrr = rr_n;
+  for (int e = wave; e < nrr; e += 4) {
+    const int ent = __builtin_amdgcn_readfirstlane((int)rr_list[e]);
+    const int gq = ent & 31, rl = ent >> 5;
+    const int r = row0 + rl;
+    // the row's elements tau*c + i = src[tau][r][h][gq*c + i], two per word (uniform loads)
+    uint32_t xw[E / 2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t* xs = reinterpret_cast<const uint32_t*>(p.src + (int64_t)r * p.stride_token +
+                                                             (int64_t)t * p.stride_loop + (int64_t)h * p.stride_head + gq * C);
+#pragma unroll
+      for (int i = 0; i < C / 2; ++i) xw[t * (C / 2) + i] = xs[i];
+    }
+    const uint16_t* cb_q = cb_h + (int64_t)gq * kCodes * E;
+    double bd = INFINITY;
+    uint32_t bk = 0u;
+#pragma unroll 1
+    for (int i = 0; i < kCodes / 64; ++i) {
+      const uint32_t k = (uint32_t)(lane + 64 * i);
+      u32x4 cv[E / 8];
+#pragma unroll
+      for (int e8 = 0; e8 < E / 8; ++e8) cv[e8] = reinterpret_cast<const u32x4*>(cb_q + k * E)[e8];
+      double dd = 0.0;
+      {
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int e2 = 0; e2 < E / 2; ++e2) {
+          const uint32_t cw = cv[e2 >> 2][e2 & 3];
+          const double d0 = (double)bf16_lo(xw[e2]) - (double)bf16_lo(cw);
+          dd = dd + d0 * d0;
+          const double d1 = (double)bf16_hi(xw[e2]) - (double)bf16_hi(cw);
+          dd = dd + d1 * d1;
+        }
+      }
+      if (dd < bd) {   // k grows with i: a strict comparison keeps the lowest index
+        bd = dd;
+        bk = k;
+      }
+    }
+    // wave minimum of (distance, index)
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double od = __shfl_xor(bd, off, 64);
+      const uint32_t ok2 = __shfl_xor(bk, off, 64);
+      if (od < bd || (od == bd && ok2 < bk)) {
+        bd = od;
+        bk = ok2;
+      }
+    }
+    if (lane == 0) {
+      if (p.out_idx) p.out_idx[((int64_t)r * p.Hkv + h) * NG + gq] = (int)bk;
+      const int64_t sl = slot_of(r);
+      if (sl >= 0) pool_h[sl + (gq >> 2) * 16 + (gq & 3)] = (uint8_t)bk;
+      if (p.rerank_count) atomicAdd(p.rerank_count, 1ull);
     }
   }
 }
@@ -475,6 +504,7 @@ hipError_t launch_encode(const EncodeParams& p, int c, hipStream_t stream) {
   const dim3 grid((unsigned)blocks);
   // the staged bulk path takes 64 channels at a time
   if (!small && (p.NG * c) % kStageCh != 0) return hipErrorInvalidValue;
+  if (p.NG > kMaxGroups) return hipErrorInvalidValue;
   if (c == 4 && small)
     hipLaunchKernelGGL((encode_kernel<4, 2, false>), grid, dim3(256), 0, stream, p, groups_per_wg, gx, gy);
   else if (c == 4)
