@@ -2,9 +2,10 @@
 
 One step = one decode step of a looped transformer stack over a packed,
 loop-axis vector-quantized KV cache: for every loop step t (outer) and layer l
-(inner), one decode-attention launch over all B sequences x Hq heads; then, per
-(layer, loop group, K/V), the encode of the B tokens that leave the bf16 recent
-window (written to a fixed VQ position so the cache stays the same size).
+(inner), one decode-attention launch over all B sequences x Hq heads; then one
+eviction launch that encodes, for every layer, loop group and K/V, the B tokens
+that leave the bf16 recent window (written to a fixed VQ position so the cache
+stays the same size).
 
 Default workload: 24 layers x 4 loop steps, 16 heads, head_dim 128, batch 64,
 32768-token context, 0.5 bit/elem (c=4, G=4, 8-bit indices), 8 prefix + 64 recent
@@ -137,8 +138,8 @@ class Bench:
         self.ws_bytes = lvq.loopvq_decode_attn_workspace(self.cfg, B, wl.context)
         self.ws = torch.empty(max(16, self.ws_bytes), dtype=torch.uint8, device=dev)
         self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
-        self.evict_seq = torch.arange(B, dtype=torch.int32, device=dev)
         self.evict_pos = torch.full((B,), n_vq - 1, dtype=torch.int32, device=dev)
+        self.evict_slot = torch.zeros((B,), dtype=torch.int32, device=dev)
         self.setup_s = time.time() - t0
         log(f"setup done in {self.setup_s:.1f}s; re-ranked sub-vectors during build: {int(self.rerank.item())}")
 
@@ -151,18 +152,17 @@ class Bench:
             v_prefix=self.pre[1, l, t], k_recent=self.rec[0, l, t], v_recent=self.rec[1, l, t], rot=self.rot,
             workspace=self.ws, workspace_bytes=self.ws_bytes)
 
-    def evict(self, l, j, kind, slot=0):
-        """Encode the token leaving the recent window of every sequence (ring slot `slot`)."""
+    def evict(self):
+        """Encode the token leaving the recent window of every sequence (ring slot 0), for every layer,
+        loop group and kind, in one launch."""
         wl = self.wl
-        B, H, R, d, T = wl.batch, wl.kv_heads, wl.recent, wl.head_dim, wl.loops
-        src = self.rec[kind, l, j * wl.loop_group]
-        self.lvq.loopvq_encode(self.cfg, layer=l, loop_group=j, kind=kind, n_tokens=B,
-                               src=src.data_ptr() + slot * d * 2, stride_loop=B * H * R * d, stride_token=H * R * d,
-                               stride_head=R * d, seq_id=self.evict_seq, vq_pos=self.evict_pos, block_table=self.bt,
-                               batch=B, max_pages_per_seq=self.pages_per_seq, num_pages=self.num_pages,
-                               cb=self.cb[kind], cb_norms=self.norms[kind], pool=self.pool)
+        self.lvq.loopvq_evict(self.cfg, batch=wl.batch, max_pages_per_seq=self.pages_per_seq,
+                              num_pages=self.num_pages, k_ring=self.rec[0], v_ring=self.rec[1],
+                              ring_slot=self.evict_slot, vq_pos=self.evict_pos, block_table=self.bt,
+                              cb_k=self.cb[0], cb_v=self.cb[1], norms_k=self.norms[0], norms_v=self.norms[1],
+                              pool=self.pool)
 
-    def step(self, events=None):
+    def step(self, events=None, evict_events=None):
         wl = self.wl
         E = self.torch.cuda.Event
         for t in range(wl.loops):
@@ -175,10 +175,14 @@ class Bench:
                     events.append((e0, e1))
                 else:
                     self.decode(l, t)
-        for l in range(wl.layers):
-            for j in range(wl.loop_groups):
-                for kind in (0, 1):
-                    self.evict(l, j, kind)
+        if evict_events is not None:
+            e0, e1 = E(enable_timing=True), E(enable_timing=True)
+            e0.record()
+            self.evict()
+            e1.record()
+            evict_events.append((e0, e1))
+        else:
+            self.evict()
 
 
 def cpu_baseline(wl, seconds: float) -> dict:
@@ -408,8 +412,9 @@ def main():
     t0 = time.perf_counter()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
+    evict_events = []
     for _ in range(args.steps):
-        bench.step(events)
+        bench.step(events, evict_events)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -433,12 +438,14 @@ def main():
                    "chans_per_group": wl.chans, "index_bits": wl.index_bits,
                    "bits_per_elem": wl.index_bits / (wl.chans * wl.loop_group), "page_tokens": wl.page_tokens,
                    "launches_per_step": wl.layers * wl.loops,
-                   "eviction_encodes_per_step": wl.layers * wl.loop_groups * 2},
+                   "eviction_launches_per_step": 1,
+                   "evicted_sub_vectors_per_step": wl.layers * wl.loop_groups * 2 * wl.batch * wl.kv_heads * wl.groups},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
         "decode_launch_us": {"mean": avg_us, "p10": float(np.percentile(launch_us, 10)),
                              "p50": float(np.percentile(launch_us, 50)), "p90": float(np.percentile(launch_us, 90))},
         "algorithmic_bytes_per_launch": ab,
+        "evict_launch_us": float(np.mean([a.elapsed_time(b) * 1e3 for a, b in evict_events])),
         "step_gbps": ab["total"] * wl.layers * wl.loops / (step_ms * 1e-3) / 1e9,
     }
     if not args.no_cpu_baseline:

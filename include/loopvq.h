@@ -157,6 +157,39 @@ typedef struct loopvq_encode_args {
 
 loopvq_status loopvq_encode(const loopvq_config* cfg, const loopvq_encode_args* args, void* stream);
 
+/* Evict: when a new token enters the bf16 recent window of R tokens (airadar.tv
+ * summary, section "Utilisation"), the oldest one leaves it and is vector-
+ * quantized.  One call encodes that token for every layer, loop group, kind
+ * (K and V), kv-head and channel group, exactly as loopvq_encode would, in a
+ * single launch (the same screen and exact re-rank).
+ * The recent windows are rings: k_ring / v_ring hold bf16
+ *   [L][T][B][Hkv][R][d]   (the per-(layer, loop step) window of decode is
+ *                           k_ring + (l*T + t) * B*Hkv*R*d),
+ * and the leaving token of sequence b is in slot ring_slot[b] of every
+ * (layer, loop step, kv-head) ring.  Its indices are written at vq position
+ * vq_pos[b] of sequence b in the pool.  A sequence is skipped when
+ * vq_pos[b] < 0 or ring_slot[b] is outside [0, R).  After the call returns (on
+ * the stream) the caller may overwrite the slot with the incoming token. */
+typedef struct loopvq_evict_args {
+  int32_t batch;                /* B: sequences (rows of ring_slot, vq_pos, block_table) */
+  int32_t max_pages_per_seq;
+  int64_t num_pages;            /* pages per (layer, loop group, kv-head) in the pool */
+  const uint16_t* k_ring;       /* device bf16 [L][T][B][Hkv][R][d], 16-byte aligned */
+  const uint16_t* v_ring;       /* device bf16, same layout */
+  const int32_t* ring_slot;     /* device [B] */
+  const int32_t* vq_pos;        /* device [B] */
+  const int32_t* block_table;   /* device [B][max_pages_per_seq] */
+  const uint16_t* cb_k;         /* device canonical key codebooks */
+  const uint16_t* cb_v;         /* device canonical value codebooks */
+  const float* norms_k;         /* device squared norms of the key codebooks */
+  const float* norms_v;
+  uint8_t* pool;                /* device index pool (written) */
+  int32_t* out_idx;             /* optional device [L][J][2][B][Hkv][NG] copy of the chosen indices */
+  unsigned long long* rerank_count; /* optional device counter: += sub-vectors re-scored in fp64 */
+} loopvq_evict_args;
+
+loopvq_status loopvq_evict(const loopvq_config* cfg, const loopvq_evict_args* args, void* stream);
+
 /* Decode attention for one (layer l, loop step t) over all B sequences and Hq
  * query heads: for query (b, hq) with kv-head h = hq / (Hq/Hkv) and N =
  * seq_lens[b] cached tokens (the token being decoded included), the keys and

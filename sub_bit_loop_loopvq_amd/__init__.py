@@ -47,6 +47,12 @@ class loopvq_encode_args(ctypes.Structure):
                 ("pool", _P), ("out_idx", _P), ("rerank_count", _P)]
 
 
+class loopvq_evict_args(ctypes.Structure):
+    _fields_ = [("batch", _I32), ("max_pages_per_seq", _I32), ("num_pages", _I64), ("k_ring", _P), ("v_ring", _P),
+                ("ring_slot", _P), ("vq_pos", _P), ("block_table", _P), ("cb_k", _P), ("cb_v", _P),
+                ("norms_k", _P), ("norms_v", _P), ("pool", _P), ("out_idx", _P), ("rerank_count", _P)]
+
+
 class loopvq_decode_args(ctypes.Structure):
     _fields_ = [("layer", _I32), ("loop", _I32), ("batch", _I32), ("max_pages_per_seq", _I32),
                 ("max_seq_len", _I32), ("num_splits", _I32), ("num_pages", _I64),
@@ -57,8 +63,8 @@ class loopvq_decode_args(ctypes.Structure):
 
 
 EXPORTS = ("loopvq_config_check", "loopvq_bits_per_elem", "loopvq_layout_query", "loopvq_codebook_prepare",
-           "loopvq_encode", "loopvq_decode_attn_workspace", "loopvq_decode_attn", "loopvq_status_string",
-           "loopvq_last_error")
+           "loopvq_encode", "loopvq_evict", "loopvq_decode_attn_workspace", "loopvq_decode_attn",
+           "loopvq_status_string", "loopvq_last_error")
 
 _lib = None
 
@@ -79,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.loopvq_codebook_prepare.argtypes, L.loopvq_codebook_prepare.restype = [cfgp, _P, _P, _P, _P], _I32
         L.loopvq_encode.argtypes = [cfgp, ctypes.POINTER(loopvq_encode_args), _P]
         L.loopvq_encode.restype = _I32
+        L.loopvq_evict.argtypes = [cfgp, ctypes.POINTER(loopvq_evict_args), _P]
+        L.loopvq_evict.restype = _I32
         L.loopvq_decode_attn_workspace.argtypes = [cfgp, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]
         L.loopvq_decode_attn_workspace.restype = _I32
         L.loopvq_decode_attn.argtypes = [cfgp, ctypes.POINTER(loopvq_decode_args), _P, ctypes.c_size_t, _P]
@@ -169,6 +177,16 @@ def loopvq_encode(cfg, *, layer, loop_group, kind, n_tokens, src, stride_loop, s
                            cb_norms=_ptr(cb_norms), pool=_ptr(pool), out_idx=_ptr(out_idx),
                            rerank_count=_ptr(rerank_count))
     _check(lib().loopvq_encode(ctypes.byref(cfg), ctypes.byref(a), _stream(stream)))
+
+
+def loopvq_evict(cfg, *, batch, max_pages_per_seq, num_pages, k_ring, v_ring, ring_slot, vq_pos, block_table, cb_k,
+                 cb_v, norms_k, norms_v, pool, out_idx=None, rerank_count=None, stream=None) -> None:
+    a = loopvq_evict_args(batch=batch, max_pages_per_seq=max_pages_per_seq, num_pages=num_pages,
+                          k_ring=_ptr(k_ring), v_ring=_ptr(v_ring), ring_slot=_ptr(ring_slot), vq_pos=_ptr(vq_pos),
+                          block_table=_ptr(block_table), cb_k=_ptr(cb_k), cb_v=_ptr(cb_v), norms_k=_ptr(norms_k),
+                          norms_v=_ptr(norms_v), pool=_ptr(pool), out_idx=_ptr(out_idx),
+                          rerank_count=_ptr(rerank_count))
+    _check(lib().loopvq_evict(ctypes.byref(cfg), ctypes.byref(a), _stream(stream)))
 
 
 def loopvq_decode_attn_workspace(cfg, batch: int, max_seq_len: int) -> int:

@@ -118,6 +118,27 @@ int plan_splits(const loopvq_config* c, int32_t batch, int32_t max_seq_len) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(S, 256));
 }
 
+// Fields of an encode launch that depend only on the config and the pool.
+lvq::EncodeParams encode_params(const loopvq_config* cfg, const Sizes& z, int32_t batch, int32_t max_pages,
+                                int64_t num_pages) {
+  lvq::EncodeParams p{};
+  p.L = cfg->num_layers;
+  p.J = z.J;
+  p.Jcb = z.Jcb;
+  p.T = cfg->num_loops;
+  p.Hkv = cfg->num_kv_heads;
+  p.NG = z.ng;
+  p.G = cfg->loop_group;
+  p.pt_shift = ilog2(cfg->page_tokens);
+  p.max_pages = max_pages;
+  p.batch = batch;
+  p.num_pages = num_pages;
+  p.page_bytes = z.page_bytes;
+  p.kind_bytes = z.kind_bytes;
+  p.head_stride = num_pages * z.page_bytes;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -198,20 +219,12 @@ loopvq_status loopvq_encode(const loopvq_config* cfg, const loopvq_encode_args* 
   if (a->out_idx && !aligned(a->out_idx, 4)) return fail(LOOPVQ_ERR_MISALIGNED, "out_idx must be 4-byte aligned");
   if (a->rerank_count && !aligned(a->rerank_count, 8))
     return fail(LOOPVQ_ERR_MISALIGNED, "rerank_count must be 8-byte aligned");
-  const int jcb = cfg->codebook_per_loop_group ? a->loop_group : 0;
-  lvq::EncodeParams p{};
-  p.n_tokens = a->n_tokens;
-  p.Hkv = cfg->num_kv_heads;
-  p.NG = z.ng;
-  p.G = cfg->loop_group;
-  p.pt_shift = ilog2(cfg->page_tokens);
-  p.max_pages = a->max_pages_per_seq;
-  p.batch = a->batch;
+  lvq::EncodeParams p = encode_params(cfg, z, a->batch, a->max_pages_per_seq, a->num_pages);
+  p.n_slices = 1;
+  p.layer = a->layer;
+  p.loop_group = a->loop_group;
   p.kind = a->kind;
-  p.num_pages = a->num_pages;
-  p.page_bytes = z.page_bytes;
-  p.kind_bytes = z.kind_bytes;
-  p.head_stride = a->num_pages * z.page_bytes;
+  p.n_tokens = a->n_tokens;
   p.src = a->src;
   p.stride_loop = a->stride_loop;
   p.stride_token = a->stride_token;
@@ -219,14 +232,65 @@ loopvq_status loopvq_encode(const loopvq_config* cfg, const loopvq_encode_args* 
   p.seq_id = a->seq_id;
   p.vq_pos = a->vq_pos;
   p.block_table = a->block_table;
-  const int64_t set0 = (int64_t(a->layer) * z.Jcb + jcb) * cfg->num_kv_heads;
-  p.cb_lj = a->cb + set0 * z.ng * z.K * z.E;
-  p.norms_lj = a->cb_norms + set0 * z.ng * z.K;
-  p.pool_lj = a->pool + (int64_t(a->layer) * z.J + a->loop_group) * cfg->num_kv_heads * p.head_stride;
+  // the kernel takes the kind-1 codebook fields for kind 1: an encode's one codebook serves both
+  p.cb = p.cb_v = a->cb;
+  p.norms = p.norms_v = a->cb_norms;
+  p.src_v = a->src;
+  p.pool = a->pool;
   p.out_idx = a->out_idx;
   p.rerank_count = a->rerank_count;
   const hipError_t e = lvq::launch_encode(p, cfg->chans_per_group, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LOOPVQ_ERR_HIP, "encode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+loopvq_status loopvq_evict(const loopvq_config* cfg, const loopvq_evict_args* a, void* stream) {
+  loopvq_status s = check_config(cfg);
+  if (s) return s;
+  if (!a) return fail(LOOPVQ_ERR_INVALID_ARG, "args is NULL");
+  if ((s = check_supported(cfg))) return s;
+  const Sizes z = sizes_of(cfg);
+  if (cfg->recent_tokens < 1) return fail(LOOPVQ_ERR_INVALID_ARG, "eviction needs recent_tokens >= 1");
+  if (a->batch < 1 || a->max_pages_per_seq < 1 || a->num_pages < 1)
+    return fail(LOOPVQ_ERR_INVALID_ARG, "batch, max_pages_per_seq and num_pages must be >= 1");
+  if (!a->k_ring || !a->v_ring || !a->ring_slot || !a->vq_pos || !a->block_table || !a->cb_k || !a->cb_v ||
+      !a->norms_k || !a->norms_v || !a->pool)
+    return fail(LOOPVQ_ERR_INVALID_ARG,
+                "k_ring, v_ring, ring_slot, vq_pos, block_table, cb_k, cb_v, norms_k, norms_v and pool must not be "
+                "NULL");
+  if (!aligned(a->k_ring, 16) || !aligned(a->v_ring, 16))
+    return fail(LOOPVQ_ERR_MISALIGNED, "k_ring and v_ring must be 16-byte aligned");
+  if (!aligned(a->cb_k, 16) || !aligned(a->cb_v, 16) || !aligned(a->norms_k, 16) || !aligned(a->norms_v, 16))
+    return fail(LOOPVQ_ERR_MISALIGNED, "codebooks and norms must be 16-byte aligned");
+  if (a->out_idx && !aligned(a->out_idx, 4)) return fail(LOOPVQ_ERR_MISALIGNED, "out_idx must be 4-byte aligned");
+  if (a->rerank_count && !aligned(a->rerank_count, 8))
+    return fail(LOOPVQ_ERR_MISALIGNED, "rerank_count must be 8-byte aligned");
+  if (int64_t(cfg->num_layers) * z.J * 2 * cfg->num_kv_heads * (z.ng / 4) > (int64_t(1) << 31) - 1)
+    return fail(LOOPVQ_ERR_INVALID_ARG, "too many slices for one launch");
+  const int64_t R = cfg->recent_tokens, d = cfg->head_dim;
+  lvq::EncodeParams p = encode_params(cfg, z, a->batch, a->max_pages_per_seq, a->num_pages);
+  p.n_slices = cfg->num_layers * z.J * 2;
+  p.n_tokens = a->batch;
+  p.R = cfg->recent_tokens;
+  p.src = a->k_ring;
+  p.src_v = a->v_ring;
+  p.stride_head = R * d;
+  p.stride_token = cfg->num_kv_heads * R * d;          // sequence b
+  p.stride_loop = int64_t(a->batch) * p.stride_token;   // loop step t
+  p.stride_slot = d;
+  p.seq_id = nullptr;
+  p.vq_pos = a->vq_pos;
+  p.row_slot = a->ring_slot;
+  p.block_table = a->block_table;
+  p.cb = a->cb_k;
+  p.cb_v = a->cb_v;
+  p.norms = a->norms_k;
+  p.norms_v = a->norms_v;
+  p.pool = a->pool;
+  p.out_idx = a->out_idx;
+  p.rerank_count = a->rerank_count;
+  const hipError_t e = lvq::launch_encode(p, cfg->chans_per_group, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LOOPVQ_ERR_HIP, "evict launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -90,16 +90,36 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, col = lane & 31;
-  // logical block = (kv-head, row block, group block), kv-head outermost
+  // logical block = (slice, kv-head, row block, group block), slice and kv-head outermost
   const int q = xcd_local_block(blockIdx.x, gridDim.x);
   const int g0 = (q % gx) * groups_per_wg;
   const int row0 = ((q / gx) % gy) * ROWS;
-  const int h = q / (gx * gy);
+  const int h = (q / (gx * gy)) % p.Hkv;
+  const int slice = q / (gx * gy * p.Hkv);
   const int NG = p.NG;
-
-  const uint16_t* cb_h = p.cb_lj + (int64_t)h * NG * kCodes * E;
-  const float* nrm_h = p.norms_lj + (int64_t)h * NG * kCodes;
-  uint8_t* pool_h = p.pool_lj + (int64_t)h * p.head_stride;
+  int layer = p.layer, lg = p.loop_group, kind = p.kind;
+  const uint16_t* src = p.src;
+  if (p.n_slices > 1) {   // eviction: slice = (layer * J + loop group) * 2 + kind
+    kind = slice & 1;
+    lg = (slice >> 1) % p.J;
+    layer = (slice >> 1) / p.J;
+    src = (kind ? p.src_v : p.src) + (int64_t)(layer * p.T + lg * p.G) * p.stride_loop;
+  }
+  const int64_t set = ((int64_t)layer * p.Jcb + (p.Jcb > 1 ? lg : 0)) * p.Hkv + h;
+  const uint16_t* cb_h = (kind ? p.cb_v : p.cb) + set * NG * kCodes * E;
+  const float* nrm_h = (kind ? p.norms_v : p.norms) + set * NG * kCodes;
+  uint8_t* pool_h = p.pool + ((int64_t)(layer * p.J + lg) * p.Hkv + h) * p.head_stride;
+  int32_t* out_idx = p.out_idx ? p.out_idx + (int64_t)slice * p.n_tokens * p.Hkv * NG : nullptr;
+  // element offset of row r (head h, loop step 0, channel 0) in src; a ring slot outside
+  // [0, R) reads slot 0 (the row is then not stored)
+  auto row_off = [&](int r) -> int64_t {
+    int64_t o = (int64_t)r * p.stride_token + (int64_t)h * p.stride_head;
+    if (p.row_slot) {
+      const int sl = p.row_slot[r];
+      o += (int64_t)((sl >= 0 && sl < p.R) ? sl : 0) * p.stride_slot;
+    }
+    return o;
+  };
   const int pt_mask = (1 << p.pt_shift) - 1;
   const uint32_t one2 = 0x3f803f80u;   // two bf16 ones
   __shared__ __align__(16) uint8_t stage[STAGE ? 4 * ROWS * 128 : 16];
@@ -114,13 +134,14 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
   // when the row is past the end, its sequence or position is out of range or its page is
   // unmapped; group g adds (g / 4) * 16 + g % 4.  (All loads are issued unconditionally at
   // clamped addresses, then validated.)
+  auto slot_ok = [&](int r) { return !p.row_slot || (p.row_slot[r] >= 0 && p.row_slot[r] < p.R); };
   auto slot_of = [&](int r) -> int64_t {   // the same for one row, with plain loads (re-rank)
-    const int sq = p.seq_id[r], u = p.vq_pos[r];
-    if (sq < 0 || sq >= p.batch || u < 0 || (u >> p.pt_shift) >= p.max_pages) return -1;
+    const int sq = p.seq_id ? p.seq_id[r] : r, u = p.vq_pos[r];
+    if (!slot_ok(r) || sq < 0 || sq >= p.batch || u < 0 || (u >> p.pt_shift) >= p.max_pages) return -1;
     const int page = p.block_table[(int64_t)sq * p.max_pages + (u >> p.pt_shift)];
     if (page < 0 || page >= p.num_pages) return -1;
     const int w = u & pt_mask;
-    return (int64_t)page * p.page_bytes + (int64_t)p.kind * p.kind_bytes + (w >> 2) * (NG >> 2) * 16 + (w & 3) * 4;
+    return (int64_t)page * p.page_bytes + (int64_t)kind * p.kind_bytes + (w >> 2) * (NG >> 2) * 16 + (w & 3) * 4;
   };
   int64_t slot[TT];
   {
@@ -128,8 +149,8 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       const int r = min(row0 + tt * 32 + col, p.n_tokens - 1);
-      seq[tt] = p.seq_id[r];
-      u[tt] = p.vq_pos[r];
+      seq[tt] = p.seq_id ? p.seq_id[r] : r;
+      u[tt] = slot_ok(r) ? p.vq_pos[r] : -1;
     }
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
@@ -142,7 +163,7 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
       const bool ok = row0 + tt * 32 + col < p.n_tokens && seq[tt] >= 0 && seq[tt] < p.batch && u[tt] >= 0 &&
                       (u[tt] >> p.pt_shift) < p.max_pages && page[tt] >= 0 && page[tt] < p.num_pages;
       const int w = u[tt] & pt_mask;
-      slot[tt] = ok ? (int64_t)page[tt] * p.page_bytes + (int64_t)p.kind * p.kind_bytes + (w >> 2) * (NG >> 2) * 16 +
+      slot[tt] = ok ? (int64_t)page[tt] * p.page_bytes + (int64_t)kind * p.kind_bytes + (w >> 2) * (NG >> 2) * 16 +
                           (w & 3) * 4
                     : (int64_t)-1;
     }
@@ -192,8 +213,7 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
           xr[tt][m] = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
       } else {
-        const int r = min(row0 + tt * 32 + col, p.n_tokens - 1);
-        const uint16_t* base = p.src + (int64_t)r * p.stride_token + (int64_t)h * p.stride_head;
+        const uint16_t* base = src + row_off(min(row0 + tt * 32 + col, p.n_tokens - 1));
 #pragma unroll
         for (int m = 0; m < NMF; ++m) {
           if constexpr (C == 4) {
@@ -215,7 +235,7 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
   // Rows past the end read the last row.
   auto stage_rows = [&](int ch0) {
     const int sl = (lane >> 1) & 15;   // stage slot of this lane
-    const uint16_t* plane = p.src + (int64_t)wave * p.stride_loop + (int64_t)h * p.stride_head;
+    const uint16_t* plane = src + (int64_t)wave * p.stride_loop + (int64_t)h * p.stride_head;
     if (row0 + ROWS <= p.n_tokens && p.stride_token < (int64_t)1 << 30) {
       // whole block: a uniform row-pair base plus a 32-bit lane offset (which includes the
       // channel range, so that it is not kept live outside this function)
@@ -417,7 +437,7 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
     for (int tt = 0; tt < TT; ++tt) {
       const int r = row0 + tt * 32 + col;
       if (half == 0 && r < p.n_tokens && !rerank[tt]) {
-        if (p.out_idx) p.out_idx[((int64_t)r * p.Hkv + h) * NG + g] = (int)best[tt];
+        if (out_idx) out_idx[((int64_t)r * p.Hkv + h) * NG + g] = (int)best[tt];
         if (slot[tt] >= 0) pool_h[slot[tt] + (g >> 2) * 16 + (g & 3)] = (uint8_t)best[tt];
       }
     }
@@ -437,8 +457,7 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
     uint32_t xw[E / 2];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const uint32_t* xs = reinterpret_cast<const uint32_t*>(p.src + (int64_t)r * p.stride_token +
-                                                             (int64_t)t * p.stride_loop + (int64_t)h * p.stride_head + gq * C);
+      const uint32_t* xs = reinterpret_cast<const uint32_t*>(src + row_off(r) + (int64_t)t * p.stride_loop + gq * C);
 #pragma unroll
       for (int i = 0; i < C / 2; ++i) xw[t * (C / 2) + i] = xs[i];
     }
@@ -479,7 +498,7 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
       }
     }
     if (lane == 0) {
-      if (p.out_idx) p.out_idx[((int64_t)r * p.Hkv + h) * NG + gq] = (int)bk;
+      if (out_idx) out_idx[((int64_t)r * p.Hkv + h) * NG + gq] = (int)bk;
       const int64_t sl = slot_of(r);
       if (sl >= 0) pool_h[sl + (gq >> 2) * 16 + (gq & 3)] = (uint8_t)bk;
       if (p.rerank_count) atomicAdd(p.rerank_count, 1ull);
@@ -494,12 +513,13 @@ hipError_t launch_encode(const EncodeParams& p, int c, hipStream_t stream) {
   // small batches (tokens leaving the recent window): one group per wave, spread over many
   // workgroups; bulk: a workgroup owns every group of 128 rows, so each cache row is read
   // whole by one workgroup
-  const bool small = (int64_t)p.n_tokens * p.Hkv < 16384;
+  // (an eviction's rows sit at ring slots, not at a fixed row stride: always the direct path)
+  const bool small = p.n_slices > 1 || (int64_t)p.n_tokens * p.Hkv < 16384;
   const int groups_per_wg = small ? 4 : p.NG;
   const int rows_per_wg = small ? 64 : 128;
   const int gx = (p.NG + groups_per_wg - 1) / groups_per_wg;
   const int gy = (p.n_tokens + rows_per_wg - 1) / rows_per_wg;
-  const int64_t blocks = (int64_t)gx * gy * p.Hkv;
+  const int64_t blocks = (int64_t)gx * gy * p.Hkv * p.n_slices;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks);
   // the staged bulk path takes 64 channels at a time

@@ -41,17 +41,28 @@ struct DecodeParams {
 };
 
 struct EncodeParams {
-  int n_tokens, Hkv, NG, G, pt_shift, max_pages, batch, kind;
+  // One launch covers n_slices (layer, loop group, kind) slices: one (p.layer, p.loop_group,
+  // p.kind) for an encode, every slice (l, j, kind) = ((l*J + j)*2 + kind) for an eviction.
+  int n_slices, layer, loop_group, kind;
+  int L, J, Jcb, T;
+  int n_tokens, Hkv, NG, G, pt_shift, max_pages, batch;
+  int R;                     // ring slots per window (row_slot in [0, R)), eviction only
   int64_t num_pages, page_bytes, kind_bytes, head_stride;
+  // sources: an encode's src points at loop step jG of its slice; an eviction's src / src_v
+  // are the K / V window rings [L][T][B][Hkv][R][d]
   const uint16_t* src;
-  int64_t stride_loop, stride_token, stride_head;
-  const int32_t* seq_id;
-  const int32_t* vq_pos;
+  const uint16_t* src_v;
+  int64_t stride_loop, stride_token, stride_head, stride_slot;
+  const int32_t* seq_id;     // [n_tokens], or nullptr: row r is sequence r
+  const int32_t* vq_pos;     // [n_tokens]; a negative position skips the row
+  const int32_t* row_slot;   // [n_tokens] ring slot of each row, or nullptr
   const int32_t* block_table;
-  const uint16_t* cb_lj;     // canonical codebooks of (l, jcb): [Hkv][NG][K][E]
-  const float* norms_lj;     // [Hkv][NG][K]
-  uint8_t* pool_lj;          // pool + ((l*J + j)*Hkv) * head_stride
-  int32_t* out_idx;
+  const uint16_t* cb;        // canonical codebooks [L][Jcb][Hkv][NG][K][E] read for kind 0
+  const uint16_t* cb_v;      // read for kind 1 (an encode sets both to its one codebook)
+  const float* norms;        // [L][Jcb][Hkv][NG][K], kind 0
+  const float* norms_v;      // kind 1
+  uint8_t* pool;             // pool base: [L][J][Hkv][num_pages][page_bytes]
+  int32_t* out_idx;          // [n_slices][n_tokens][Hkv][NG] or nullptr
   unsigned long long* rerank_count;
 };
 

@@ -37,6 +37,7 @@ def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(lvq.loopvq_layout) == 80
     assert ctypes.sizeof(lvq.loopvq_encode_args) == 4 * 4 + 8 + 3 * 8 + 3 * 8 + 4 + 4 + 8 + 5 * 8
     assert ctypes.sizeof(lvq.loopvq_decode_args) == 6 * 4 + 8 + 10 * 8 + 8 + 8 + 8 + 8
+    assert ctypes.sizeof(lvq.loopvq_evict_args) == 4 + 4 + 8 + 12 * 8
 
 
 @pytest.mark.parametrize("wl", W.ALL, ids=[w.name for w in W.ALL])
@@ -182,6 +183,42 @@ def test_encode_rejects_before_launch(over, status):
     with pytest.raises(lvq.LoopVQError) as e:
         lvq.loopvq_encode(cfg, **_encode_kw(**over))
     assert e.value.status == status
+
+
+def _evict_kw(**over):
+    kw = dict(batch=2, max_pages_per_seq=4, num_pages=8, k_ring=FAKE, v_ring=FAKE, ring_slot=FAKE, vq_pos=FAKE,
+              block_table=FAKE, cb_k=FAKE, cb_v=FAKE, norms_k=FAKE, norms_v=FAKE, pool=FAKE, stream=0)
+    kw.update(over)
+    return kw
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(batch=0), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(num_pages=0), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(ring_slot=None), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(norms_v=None), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(v_ring=FAKE + 8), lvq.LOOPVQ_ERR_MISALIGNED),
+    (dict(cb_k=FAKE + 2), lvq.LOOPVQ_ERR_MISALIGNED),
+    (dict(out_idx=FAKE + 2), lvq.LOOPVQ_ERR_MISALIGNED),
+])
+def test_evict_rejects_before_launch(over, status):
+    cfg = lvq.make_config(W.LAYER_4K)
+    with pytest.raises(lvq.LoopVQError) as e:
+        lvq.loopvq_evict(cfg, **_evict_kw(**over))
+    assert e.value.status == status
+
+
+def test_evict_needs_a_recent_window_and_a_built_variant():
+    cfg = lvq.make_config(W.LAYER_4K)
+    cfg.recent_tokens = 0
+    with pytest.raises(lvq.LoopVQError) as e:
+        lvq.loopvq_evict(cfg, **_evict_kw())
+    assert e.value.status == lvq.LOOPVQ_ERR_INVALID_ARG
+    cfg = lvq.make_config(W.LAYER_4K)
+    cfg.index_bits = 9
+    with pytest.raises(lvq.LoopVQError) as e:
+        lvq.loopvq_evict(cfg, **_evict_kw())
+    assert e.value.status == lvq.LOOPVQ_ERR_UNSUPPORTED
 
 
 def test_codebook_prepare_rejects():
