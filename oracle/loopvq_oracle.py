@@ -277,6 +277,28 @@ def decode_query(q, k_prefix, v_prefix, idx_k, idx_v, cb_k, cb_v, k_recent, v_re
     return attention(q, keys, vals, scale, rot)
 
 
+def extend_attention(q_rows, k_prefix, v_prefix, idx_k, idx_v, cb_k, cb_v, k_recent, v_recent,
+                     k_chunk, v_chunk, tau: int, c: int, scale: float, rot=None):
+    """Chunked prefill ("extend") of M new tokens over one sequence's cache, fp64.
+
+    The serving command in [AIR] "Utilisation" names a separate prefill backend; the
+    pages say nothing more.  Reading: row i of the chunk attends over the whole cached
+    context exactly as a decode query does ([prefix | vector-quantized | recent]) plus
+    the chunk's own bf16 rows 0..i (causal inside the chunk).  Window order does not
+    matter, so the chunk rows join the recent window.  Returns (o [M][d], lse [M]).
+    """
+    M = q_rows.shape[0]
+    d = k_chunk.shape[1]
+    o = np.empty((M, d), dtype=np.float64)
+    lse = np.empty(M, dtype=np.float64)
+    for i in range(M):
+        kr = np.concatenate([k_recent, k_chunk[:i + 1]], axis=0)
+        vr = np.concatenate([v_recent, v_chunk[:i + 1]], axis=0)
+        o[i], lse[i] = decode_query(q_rows[i], k_prefix, v_prefix, idx_k, idx_v, cb_k, cb_v, kr, vr, tau, c,
+                                    scale, rot)
+    return o, lse
+
+
 def near_tie(d1: np.ndarray, d2: np.ndarray, rel: float = 1e-6) -> np.ndarray:
     """Sub-vectors whose two best distances are within rel of each other (several correct indices)."""
     return (d2 - d1) <= rel * d2

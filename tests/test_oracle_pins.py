@@ -380,3 +380,78 @@ def test_near_tie_rule():
     d1 = np.array([1.0, 1.0, 0.0, 2.0])
     d2 = np.array([1.0 + 5e-7, 1.0 + 2e-6, 0.0, 3.0])
     assert O.near_tie(d1, d2).tolist() == [True, False, True, False]
+
+
+# ---------------------------------------------------------------------------
+# Extend (chunked prefill) over the cache
+# ---------------------------------------------------------------------------
+def _extend_case(seed, n_vq=23, P=3, R=5, M=9, d=16, c=4, K=16):
+    r = _rng(seed)
+    NG = d // c
+    C, Cv = r.normal(size=(NG, K, c * 4)), r.normal(size=(NG, K, c * 4))
+    ik, iv = r.integers(0, K, (n_vq, NG)), r.integers(0, K, (n_vq, NG))
+    win = [r.normal(size=(n, d)) for n in (P, P, R, R)]
+    kc, vc = r.normal(size=(M, d)), r.normal(size=(M, d))
+    q = r.normal(size=(M, d))
+    return dict(q=q, kp=win[0], vp=win[1], kr=win[2], vr=win[3], ik=ik, iv=iv, C=C, Cv=Cv, kc=kc, vc=vc, c=c)
+
+
+def test_extend_matches_masked_softmax_over_the_explicit_cache():
+    """Row i of the chunk == softmax over [all cache rows, chunk rows 0..i] written as one masked
+    score matrix (scipy softmax over a dense mask, an independent formulation)."""
+    e = _extend_case(11)
+    tau, scale = 3, 0.35
+    o, lse = O.extend_attention(e["q"], e["kp"], e["vp"], e["ik"], e["iv"], e["C"], e["Cv"], e["kr"], e["vr"],
+                                e["kc"], e["vc"], tau, e["c"], scale)
+    # cache keys written out directly from the codebooks (no dequantize helper)
+    NG = e["C"].shape[0]
+    kq = np.concatenate([e["C"][g][e["ik"][:, g], tau * 4:tau * 4 + 4] for g in range(NG)], axis=1)
+    vq = np.concatenate([e["Cv"][g][e["iv"][:, g], tau * 4:tau * 4 + 4] for g in range(NG)], axis=1)
+    keys = np.concatenate([e["kp"], kq, e["kr"], e["kc"]])
+    vals = np.concatenate([e["vp"], vq, e["vr"], e["vc"]])
+    n_cache = len(keys) - len(e["kc"])
+    M = len(e["q"])
+    mask = np.zeros((M, len(keys)), dtype=bool)
+    mask[:, :n_cache] = True
+    for i in range(M):
+        mask[i, n_cache:n_cache + i + 1] = True
+    S = np.where(mask, scale * (e["q"] @ keys.T), -np.inf)
+    Pm = softmax(S, axis=1)
+    assert np.allclose(o, Pm @ vals, rtol=1e-12, atol=1e-13)
+    from scipy.special import logsumexp
+    assert np.allclose(lse, logsumexp(S, axis=1), rtol=1e-12)
+
+
+def test_extend_is_causal_inside_the_chunk():
+    e = _extend_case(12)
+    o, _ = O.extend_attention(e["q"], e["kp"], e["vp"], e["ik"], e["iv"], e["C"], e["Cv"], e["kr"], e["vr"],
+                              e["kc"], e["vc"], 1, e["c"], 0.3)
+    kc2, vc2 = e["kc"].copy(), e["vc"].copy()
+    kc2[5:] += 3.0
+    vc2[5:] -= 7.0
+    o2, _ = O.extend_attention(e["q"], e["kp"], e["vp"], e["ik"], e["iv"], e["C"], e["Cv"], e["kr"], e["vr"],
+                               kc2, vc2, 1, e["c"], 0.3)
+    assert np.array_equal(o[:5], o2[:5])
+    assert not np.allclose(o[5:], o2[5:])
+
+
+def test_extend_closed_forms():
+    e = _extend_case(13, n_vq=0, P=0, R=0)
+    empty = np.zeros((0, 4), dtype=np.int64)
+    d = e["q"].shape[1]
+    none = np.zeros((0, d))
+    # empty cache: the first chunk row sees only itself
+    o, lse = O.extend_attention(e["q"], none, none, empty, empty, e["C"], e["Cv"], none, none, e["kc"], e["vc"], 0,
+                                e["c"], 0.5)
+    assert np.array_equal(o[0], e["vc"][0])
+    assert lse[0] == pytest.approx(0.5 * e["q"][0] @ e["kc"][0], rel=1e-14)
+    # a zero query averages every visible value row
+    f = _extend_case(14)
+    q0 = np.zeros_like(f["q"])
+    o, lse = O.extend_attention(q0, f["kp"], f["vp"], f["ik"], f["iv"], f["C"], f["Cv"], f["kr"], f["vr"],
+                                f["kc"], f["vc"], 2, f["c"], 0.2)
+    base = np.concatenate([f["vp"], O.dequantize(f["iv"], f["Cv"], 2, f["c"]), f["vr"]])
+    for i in range(len(q0)):
+        vis = np.concatenate([base, f["vc"][:i + 1]])
+        assert np.allclose(o[i], vis.mean(axis=0), rtol=1e-13, atol=1e-14)
+        assert lse[i] == pytest.approx(np.log(len(vis)), rel=1e-14)
