@@ -236,6 +236,53 @@ loopvq_status loopvq_decode_attn_workspace(const loopvq_config* cfg, int32_t bat
 loopvq_status loopvq_decode_attn(const loopvq_config* cfg, const loopvq_decode_args* args,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Extend (chunked prefill): M new tokens of every sequence, whose keys and values are
+ * still bf16, attend over the cached context plus the chunk itself.  The serving
+ * path has a prefill backend of its own (airadar.tv summary, section
+ * "Utilisation"); the pages do not describe it.  Row i of the chunk of sequence b
+ * (query head hq, kv-head hq / (Hq/Hkv)) attends over every cached token exactly
+ * as a decode query of the same (layer, loop step) does -- [prefix | vector-
+ * quantized | recent] for N = seq_lens[b] cached tokens -- plus chunk rows 0..i
+ * (causal inside the chunk), with the same softmax scale and key rotation.
+ *   q            device bf16 [B][M][Hq][d]
+ *   k_new, v_new device bf16 [B][Hkv][M][d]: the chunk's keys (rotated like the
+ *                cache's when rot is given) and values; 16-byte aligned
+ *   chunk_lens   optional device int32 [B]: rows [0, chunk_lens[b]) of sequence b
+ *                are computed (others untouched); NULL = all M
+ *   out          device fp32 [B][M][Hq][d]
+ * The other fields mean what they mean for decode (windows of the same (l, t),
+ * pool, prepared codebooks, rot, softmax_scale).  No workspace is needed.  The
+ * kernel dequantizes 64-token tiles into LDS and runs both products on bf16 MFMAs,
+ * splitting P (and a rotated q) into two bf16 parts so they keep fp32-level
+ * accuracy. */
+typedef struct loopvq_extend_args {
+  int32_t layer;                /* l */
+  int32_t loop;                 /* t (tau = t mod G, loop group t / G) */
+  int32_t batch;                /* B */
+  int32_t chunk;                /* M >= 1 */
+  int32_t max_pages_per_seq;
+  int32_t max_seq_len;          /* upper bound of seq_lens (cached tokens) */
+  int64_t num_pages;
+  const uint16_t* q;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int32_t* seq_lens;      /* device [B] */
+  const int32_t* chunk_lens;    /* device [B] or NULL */
+  const int32_t* block_table;
+  const uint8_t* pool;
+  const uint16_t* cb_k_prep;
+  const uint16_t* cb_v_prep;
+  const uint16_t* k_prefix;
+  const uint16_t* v_prefix;
+  const uint16_t* k_recent;
+  const uint16_t* v_recent;
+  const float* rot;             /* [d][d] or NULL */
+  float softmax_scale;          /* <= 0: 1/sqrt(d) */
+  float* out;
+} loopvq_extend_args;
+
+loopvq_status loopvq_extend_attn(const loopvq_config* cfg, const loopvq_extend_args* args, void* stream);
+
 /* Static description of a status code. */
 const char* loopvq_status_string(loopvq_status s);
 

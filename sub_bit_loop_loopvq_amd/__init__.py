@@ -62,9 +62,17 @@ class loopvq_decode_args(ctypes.Structure):
                 ("out", _P), ("lse", _P)]
 
 
+class loopvq_extend_args(ctypes.Structure):
+    _fields_ = [("layer", _I32), ("loop", _I32), ("batch", _I32), ("chunk", _I32), ("max_pages_per_seq", _I32),
+                ("max_seq_len", _I32), ("num_pages", _I64), ("q", _P), ("k_new", _P), ("v_new", _P),
+                ("seq_lens", _P), ("chunk_lens", _P), ("block_table", _P), ("pool", _P), ("cb_k_prep", _P),
+                ("cb_v_prep", _P), ("k_prefix", _P), ("v_prefix", _P), ("k_recent", _P), ("v_recent", _P),
+                ("rot", _P), ("softmax_scale", _F32), ("out", _P)]
+
+
 EXPORTS = ("loopvq_config_check", "loopvq_bits_per_elem", "loopvq_layout_query", "loopvq_codebook_prepare",
            "loopvq_encode", "loopvq_evict", "loopvq_decode_attn_workspace", "loopvq_decode_attn",
-           "loopvq_status_string", "loopvq_last_error")
+           "loopvq_extend_attn", "loopvq_status_string", "loopvq_last_error")
 
 _lib = None
 
@@ -91,6 +99,8 @@ def lib() -> ctypes.CDLL:
         L.loopvq_decode_attn_workspace.restype = _I32
         L.loopvq_decode_attn.argtypes = [cfgp, ctypes.POINTER(loopvq_decode_args), _P, ctypes.c_size_t, _P]
         L.loopvq_decode_attn.restype = _I32
+        L.loopvq_extend_attn.argtypes = [cfgp, ctypes.POINTER(loopvq_extend_args), _P]
+        L.loopvq_extend_attn.restype = _I32
         L.loopvq_status_string.argtypes, L.loopvq_status_string.restype = [_I32], ctypes.c_char_p
         L.loopvq_last_error.argtypes, L.loopvq_last_error.restype = [], ctypes.c_char_p
         _lib = L
@@ -209,3 +219,18 @@ def loopvq_decode_attn(cfg, *, layer, loop, batch, q, seq_lens, max_seq_len, out
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().loopvq_decode_attn(ctypes.byref(cfg), ctypes.byref(a), _ptr(workspace), workspace_bytes,
                                     _stream(stream)))
+
+
+def loopvq_extend_attn(cfg, *, layer, loop, batch, chunk, q, k_new, v_new, seq_lens, max_seq_len, out,
+                       chunk_lens=None, block_table=None, pool=None, max_pages_per_seq=0, num_pages=0,
+                       cb_k_prep=None, cb_v_prep=None, k_prefix=None, v_prefix=None, k_recent=None, v_recent=None,
+                       rot=None, softmax_scale=0.0, stream=None) -> None:
+    a = loopvq_extend_args(layer=layer, loop=loop, batch=batch, chunk=chunk, max_pages_per_seq=max_pages_per_seq,
+                           max_seq_len=max_seq_len, num_pages=num_pages, q=_ptr(q), k_new=_ptr(k_new),
+                           v_new=_ptr(v_new), seq_lens=_ptr(seq_lens), chunk_lens=_ptr(chunk_lens),
+                           block_table=_ptr(block_table), pool=_ptr(pool), cb_k_prep=_ptr(cb_k_prep),
+                           cb_v_prep=_ptr(cb_v_prep), k_prefix=_ptr(k_prefix), v_prefix=_ptr(v_prefix),
+                           k_recent=_ptr(k_recent), v_recent=_ptr(v_recent), rot=_ptr(rot),
+                           softmax_scale=softmax_scale, out=_ptr(out))
+    _check(lib().loopvq_extend_attn(ctypes.byref(cfg), ctypes.byref(a), _stream(stream)))
+

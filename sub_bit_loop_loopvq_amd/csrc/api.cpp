@@ -391,6 +391,86 @@ loopvq_status loopvq_decode_attn(const loopvq_config* cfg, const loopvq_decode_a
   return ok();
 }
 
+loopvq_status loopvq_extend_attn(const loopvq_config* cfg, const loopvq_extend_args* a, void* stream) {
+  loopvq_status s = check_config(cfg);
+  if (s) return s;
+  if (!a) return fail(LOOPVQ_ERR_INVALID_ARG, "args is NULL");
+  if ((s = check_supported(cfg))) return s;
+  const Sizes z = sizes_of(cfg);
+  if (a->layer < 0 || a->layer >= cfg->num_layers) return fail(LOOPVQ_ERR_INVALID_ARG, "layer out of range");
+  if (a->loop < 0 || a->loop >= cfg->num_loops) return fail(LOOPVQ_ERR_INVALID_ARG, "loop out of range");
+  if (a->batch < 1 || a->chunk < 1) return fail(LOOPVQ_ERR_INVALID_ARG, "batch and chunk must be >= 1");
+  if (a->max_seq_len < 0) return fail(LOOPVQ_ERR_INVALID_ARG, "max_seq_len must be >= 0");
+  const int grp = cfg->num_q_heads / cfg->num_kv_heads;
+  const int64_t row_blocks = (int64_t(a->chunk) * grp + 127) / 128;
+  if (int64_t(a->batch) * cfg->num_kv_heads * row_blocks > (int64_t(1) << 31) - 1)
+    return fail(LOOPVQ_ERR_INVALID_ARG, "batch * kv_heads * chunk too large for one launch");
+  if (!a->q || !a->k_new || !a->v_new || !a->seq_lens || !a->out)
+    return fail(LOOPVQ_ERR_INVALID_ARG, "q, k_new, v_new, seq_lens and out must not be NULL");
+  const bool can_vq = int64_t(a->max_seq_len) > int64_t(cfg->prefix_tokens) + cfg->recent_tokens;
+  if (can_vq) {
+    if (!a->block_table || !a->pool || !a->cb_k_prep || !a->cb_v_prep)
+      return fail(LOOPVQ_ERR_INVALID_ARG, "block_table, pool and prepared codebooks must not be NULL");
+    if (a->max_pages_per_seq < 1 || a->num_pages < 1)
+      return fail(LOOPVQ_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
+    if (!aligned(a->pool, 16) || !aligned(a->cb_k_prep, 16) || !aligned(a->cb_v_prep, 16))
+      return fail(LOOPVQ_ERR_MISALIGNED, "pool and prepared codebooks must be 16-byte aligned");
+  }
+  if (cfg->prefix_tokens > 0 && (!a->k_prefix || !a->v_prefix))
+    return fail(LOOPVQ_ERR_INVALID_ARG, "prefix windows must not be NULL when prefix_tokens > 0");
+  if (cfg->recent_tokens > 0 && (!a->k_recent || !a->v_recent))
+    return fail(LOOPVQ_ERR_INVALID_ARG, "recent windows must not be NULL when recent_tokens > 0");
+  if ((a->k_prefix && !aligned(a->k_prefix, 16)) || (a->v_prefix && !aligned(a->v_prefix, 16)) ||
+      (a->k_recent && !aligned(a->k_recent, 16)) || (a->v_recent && !aligned(a->v_recent, 16)) ||
+      !aligned(a->k_new, 16) || !aligned(a->v_new, 16) || !aligned(a->q, 16))
+    return fail(LOOPVQ_ERR_MISALIGNED, "q, chunk and window buffers must be 16-byte aligned");
+  if (!aligned(a->out, 16) || (a->rot && !aligned(a->rot, 4)) || !aligned(a->seq_lens, 4) ||
+      (a->chunk_lens && !aligned(a->chunk_lens, 4)))
+    return fail(LOOPVQ_ERR_MISALIGNED, "out (16 bytes), rot, seq_lens or chunk_lens misaligned");
+
+  const int j = a->loop / cfg->loop_group;
+  const int jcb = cfg->codebook_per_loop_group ? j : 0;
+  lvq::ExtendParams p{};
+  p.B = a->batch;
+  p.Hq = cfg->num_q_heads;
+  p.Hkv = cfg->num_kv_heads;
+  p.P = cfg->prefix_tokens;
+  p.R = cfg->recent_tokens;
+  p.G = cfg->loop_group;
+  p.M = a->chunk;
+  p.row_blocks = (int)row_blocks;
+  p.pt_shift = ilog2(cfg->page_tokens);
+  p.max_pages = can_vq ? a->max_pages_per_seq : 0;
+  p.max_seq_len = a->max_seq_len;
+  p.tau = a->loop % cfg->loop_group;
+  p.num_pages = a->num_pages;
+  p.page_bytes = z.page_bytes;
+  p.kind_bytes = z.kind_bytes;
+  p.head_stride = a->num_pages * z.page_bytes;
+  const float scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / std::sqrt(float(cfg->head_dim));
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.q = a->q;
+  p.k_new = a->k_new;
+  p.v_new = a->v_new;
+  p.seq_lens = a->seq_lens;
+  p.chunk_lens = a->chunk_lens;
+  p.block_table = a->block_table;
+  p.pool_lj = can_vq ? a->pool + (int64_t(a->layer) * z.J + j) * cfg->num_kv_heads * p.head_stride : nullptr;
+  const int64_t set0 = (int64_t(a->layer) * z.Jcb + jcb) * cfg->num_kv_heads;
+  const int64_t set_elems = int64_t(cfg->loop_group) * z.K * cfg->head_dim;
+  p.cbk = can_vq ? a->cb_k_prep + set0 * set_elems : nullptr;
+  p.cbv = can_vq ? a->cb_v_prep + set0 * set_elems : nullptr;
+  p.k_prefix = a->k_prefix;
+  p.v_prefix = a->v_prefix;
+  p.k_recent = a->k_recent;
+  p.v_recent = a->v_recent;
+  p.rot = a->rot;
+  p.out = a->out;
+  const hipError_t e = lvq::launch_extend(p, z.ng, cfg->chans_per_group, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LOOPVQ_ERR_HIP, "extend_attn launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* loopvq_status_string(loopvq_status s) {
   switch (s) {
     case LOOPVQ_OK: return "ok";

@@ -1,0 +1,326 @@
+// LoopVQ extend (chunked prefill) attention over the packed, loop-axis vector-quantized cache (gfx950).
+//
+// What it computes (airadar.tv summary of LoopVQ, section "Utilisation": the serving path
+// keeps P prefix and R recent tokens in bf16 and has its own prefill backend; section
+// "Raisons": indices are stored packed).  For one (layer, loop step), chunk row i of
+// sequence b (query head hq, kv-head h = hq / (Hq / Hkv)) attends over every cached token,
+// [bf16 prefix | vector-quantized rows | bf16 recent] exactly as a decode query does, plus the
+// chunk's own bf16 rows 0..i.  A vector-quantized row's channels g*c .. g*c+c-1 are the
+// loop-step-tau slice of codeword idx[n][g] of (layer, kv-head, group g).
+//
+// How (MI355X):
+//  * workgroup = 128 query rows (row = (chunk token, q-head of the kv-head)) of one
+//    (sequence, kv-head); 4 waves of 32 rows.  Keys come in tiles of 64 tokens.
+//  * each tile is staged in LDS by the whole workgroup: K as [token][d] bf16 rows and V
+//    transposed as [d][token] bf16 (rows padded so the MFMA operand reads hit distinct banks).
+//    Vector-quantized tokens are dequantized on the way: the packed index byte of (token,
+//    group) selects c channels of the loop-step slice of the prepared codebook.
+//  * per wave: S^T = K Q^T on bf16 32x32x16 MFMAs (a rotated q' = R^T q is split into two
+//    bf16 parts, two MFMAs), online softmax in log2 units with the causal mask of the
+//    chunk, then O^T += V^T P^T with P split into two bf16 parts (hi + lo, 2^-16 relative),
+//    so the products keep fp32-level accuracy.  The D-layout of S^T (lane = query row,
+//    registers = tokens) is directly the B operand of the second product once its 16
+//    tokens are taken in the order the registers hold them; the V^T operand reads the same
+//    order.
+#include "lvq_common.h"
+
+namespace lvq {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kKT = 64;        // keys per tile
+constexpr int kRows = 128;     // query rows per workgroup
+constexpr int kVRow = kKT + 4; // bf16 per transposed V row (8 B of padding)
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// round-to-nearest-even fp32 -> bf16 bits (finite inputs)
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+// v -> bf16 pair (hi, lo) with hi + lo == v to 2^-16 relative
+__device__ __forceinline__ void split2(float v, uint32_t& hi, uint32_t& lo) {
+  hi = bf16_rne(v);
+  lo = bf16_rne(v - __uint_as_float(hi << 16));
+}
+
+template <int NG, int C>
+__global__ void __launch_bounds__(256) extend_kernel(ExtendParams p) {
+  constexpr int D = NG * C;
+  constexpr int KROW = D + 8;         // bf16 per K row (16 B of padding)
+  constexpr int KSTEPS = D / 16;      // k-steps of S^T = K Q^T
+  constexpr int DB = D / 32;          // 32-channel blocks of O^T
+  __shared__ __align__(16) uint16_t ks[kKT * KROW];
+  __shared__ __align__(16) uint16_t vt[D * kVRow];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, col = lane & 31;
+  const int grp = p.Hq / p.Hkv;
+  const int rb = blockIdx.x % p.row_blocks;
+  const int bh = blockIdx.x / p.row_blocks;
+  const int h = bh % p.Hkv, b = bh / p.Hkv;
+
+  // context split of the cached tokens (as in decode) and this sequence's chunk length
+  int N = p.seq_lens[b];
+  N = N < 0 ? 0 : (N > p.max_seq_len ? p.max_seq_len : N);
+  const int n_prefix = N < p.P ? N : p.P;
+  int n_vq = N - p.P - p.R;
+  n_vq = n_vq < 0 ? 0 : n_vq;
+  if (n_vq > (p.max_pages << p.pt_shift)) n_vq = p.max_pages << p.pt_shift;
+  const int n_recent = N - n_prefix - n_vq;
+  int Mb = p.chunk_lens ? p.chunk_lens[b] : p.M;
+  Mb = Mb < 0 ? 0 : (Mb > p.M ? p.M : Mb);
+
+  const int row_ws = rb * kRows;                  // first row of the workgroup
+  if (row_ws / grp >= Mb) return;                 // no active row (uniform over the workgroup)
+  const int i_last = min(Mb - 1, (row_ws + kRows - 1) / grp);
+
+  // ---- this lane's query row and its q operand (B of S^T = K Q^T) --------------------------
+  const int row = row_ws + wave * 32 + col;
+  const int qi = row / grp;                       // chunk token of the row
+  const int hq = h * grp + row % grp;
+  const bool active = qi < Mb;
+  const uint16_t* qrow = p.q + (((int64_t)b * p.M + (active ? qi : 0)) * p.Hq + hq) * D;
+  u32x4 bq[KSTEPS], bq_lo[KSTEPS];
+  if (p.rot) {
+    // q' = R^T q in fp32 for the 8 channels 16kk + 8*half + j this lane supplies, split in two
+#pragma unroll 1
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      const int d0 = 16 * kk + 8 * half;
+#pragma unroll 4
+      for (int e = 0; e < D; ++e) {
+        const float qe = bf16_at(qrow + e);
+        const float* re = p.rot + (int64_t)e * D + d0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(re[j], qe, acc[j]);
+      }
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) split2(acc[j], hi[j], lo[j]);
+      bq[kk] = u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
+      bq_lo[kk] = u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      bq[kk] = *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * half);
+      bq_lo[kk] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int64_t bhk = (int64_t)b * p.Hkv + h;
+  const uint8_t* pool_h = p.pool_lj ? p.pool_lj + (int64_t)h * p.head_stride : nullptr;
+  const int pt_mask = (1 << p.pt_shift) - 1;
+  const uint16_t* slice_k = p.cbk ? p.cbk + ((int64_t)h * p.G + p.tau) * kCodes * D : nullptr;
+  const uint16_t* slice_v = p.cbv ? p.cbv + ((int64_t)h * p.G + p.tau) * kCodes * D : nullptr;
+
+  // ---- staging -----------------------------------------------------------------------------
+  // bf16 rows: token t of the tile is row r0 + t of a [rows][D] window (t < count), else zeros
+  auto stage_rows = [&](const uint16_t* kw, const uint16_t* vw, int count) {
+    constexpr int PIECES = D / 8;                 // 16-byte pieces per row
+    for (int it = tid; it < kKT * PIECES; it += 256) {
+      const int t = it / PIECES, pc = it % PIECES;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (t < count) {
+        kv = *reinterpret_cast<const u32x4*>(kw + (int64_t)t * D + 8 * pc);
+        vv = *reinterpret_cast<const u32x4*>(vw + (int64_t)t * D + 8 * pc);
+      }
+      *reinterpret_cast<u32x4*>(ks + t * KROW + 8 * pc) = kv;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        vt[(8 * pc + 2 * w) * kVRow + t] = (uint16_t)(vv[w] & 0xffffu);
+        vt[(8 * pc + 2 * w + 1) * kVRow + t] = (uint16_t)(vv[w] >> 16);
+      }
+    }
+  };
+  // vector-quantized tokens u0 .. u0 + 63 (u < n_vq), dequantized from the loop-step slices
+  auto stage_vq = [&](int u0) {
+    for (int it = tid; it < kKT * (NG / 4); it += 256) {
+      const int t = it % kKT, gq = it / kKT;     // token, group quad
+      const int u = u0 + t;
+      uint32_t ik = 0u, iv = 0u;
+      bool ok = u < n_vq;
+      if (ok) {
+        int page = p.block_table[(int64_t)b * p.max_pages + (u >> p.pt_shift)];
+        ok = page >= 0 && page < p.num_pages;
+        if (ok) {
+          const int w = u & pt_mask;
+          const uint8_t* tile = pool_h + (int64_t)page * p.page_bytes + (((w >> 2) * (NG / 4) + gq) * 16 + (w & 3) * 4);
+          ik = *reinterpret_cast<const uint32_t*>(tile);
+          iv = *reinterpret_cast<const uint32_t*>(tile + p.kind_bytes);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int g = 4 * gq + r;
+        const uint32_t kx = (ik >> (8 * r)) & 0xffu, vx = (iv >> (8 * r)) & 0xffu;
+        uint32_t kw[C / 2], vw[C / 2];
+        if (ok) {
+          const uint32_t* kc = reinterpret_cast<const uint32_t*>(slice_k + kx * D + g * C);
+          const uint32_t* vc = reinterpret_cast<const uint32_t*>(slice_v + vx * D + g * C);
+#pragma unroll
+          for (int e = 0; e < C / 2; ++e) {
+            kw[e] = kc[e];
+            vw[e] = vc[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < C / 2; ++e) kw[e] = vw[e] = 0u;
+        }
+        uint32_t* kd = reinterpret_cast<uint32_t*>(ks + t * KROW + g * C);
+#pragma unroll
+        for (int e = 0; e < C / 2; ++e) {
+          kd[e] = kw[e];
+          vt[(g * C + 2 * e) * kVRow + t] = (uint16_t)(vw[e] & 0xffffu);
+          vt[(g * C + 2 * e + 1) * kVRow + t] = (uint16_t)(vw[e] >> 16);
+        }
+      }
+    }
+  };
+
+  // ---- one staged tile: scores, online softmax, value products --------------------------------
+  // chunk_j0 >= 0 marks chunk keys: key t is chunk token chunk_j0 + t (causal); count = valid keys
+  auto consume = [&](int count, int chunk_j0) {
+    f32x16 s[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x16 acc = {};
+      const uint16_t* krow = ks + (32 * mb + col) * KROW + 8 * half;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + 16 * kk);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bq[kk]), acc, 0, 0, 0);
+        if (p.rot) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bq_lo[kk]), acc, 0, 0, 0);
+      }
+      s[mb] = acc;
+    }
+    // mask and scale (log2 units); token of register r of block mb: 32mb + 8(r/4) + 4half + r%4
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * mb + 8 * (r >> 2) + 4 * half + (r & 3);
+        const bool vis = active && t < count && (chunk_j0 < 0 || chunk_j0 + t <= qi);
+        const float v = vis ? s[mb][r] * p.scale_log2 : -INFINITY;
+        s[mb][r] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    // (no early exit: every lane takes part in the MFMAs; a row with nothing visible yet keeps
+    // m = -inf and adds zeros, using 0 as its reference so that no -inf - -inf appears)
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // m_run = -inf -> 0
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(s[mb][r] - m_use);   // -inf -> 0
+        s[mb][r] = e;
+        psum += e;
+      }
+    }
+    l_run = fmaf(l_run, alpha, psum);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    // O^T += V^T P^T over 4 k-steps of 16 keys
+#pragma unroll
+    for (int kst = 0; kst < kKT / 16; ++kst) {
+      const int mb = kst >> 1, r0 = 8 * (kst & 1);
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) split2(s[mb][r0 + j], hi[j], lo[j]);
+      const u32x4 bh = {hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
+      const u32x4 bl = {lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint16_t* vrow = vt + (32 * db + col) * kVRow + 16 * kst + 4 * half;
+        const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 8);
+        const u32x4 a = {v0.x, v0.y, v1.x, v1.y};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bh), o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bl), o[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- the key segments: prefix, vector-quantized, recent, the chunk itself (causal) ----------
+  const uint16_t* kp = p.k_prefix + bhk * p.P * D;
+  const uint16_t* vp = p.v_prefix + bhk * p.P * D;
+  for (int t0 = 0; t0 < n_prefix; t0 += kKT) {
+    __syncthreads();
+    stage_rows(kp + (int64_t)t0 * D, vp + (int64_t)t0 * D, n_prefix - t0);
+    __syncthreads();
+    consume(n_prefix - t0, -1);
+  }
+  for (int u0 = 0; u0 < n_vq; u0 += kKT) {
+    __syncthreads();
+    stage_vq(u0);
+    __syncthreads();
+    consume(n_vq - u0, -1);
+  }
+  const uint16_t* kr = p.k_recent + bhk * p.R * D;
+  const uint16_t* vr = p.v_recent + bhk * p.R * D;
+  for (int t0 = 0; t0 < n_recent; t0 += kKT) {
+    __syncthreads();
+    stage_rows(kr + (int64_t)t0 * D, vr + (int64_t)t0 * D, n_recent - t0);
+    __syncthreads();
+    consume(n_recent - t0, -1);
+  }
+  const uint16_t* kc = p.k_new + bhk * p.M * D;
+  const uint16_t* vc = p.v_new + bhk * p.M * D;
+  for (int j0 = 0; j0 <= i_last; j0 += kKT) {
+    __syncthreads();
+    stage_rows(kc + (int64_t)j0 * D, vc + (int64_t)j0 * D, i_last + 1 - j0);
+    __syncthreads();
+    consume(i_last + 1 - j0, j0);
+  }
+
+  // ---- normalise and write: O^T register r of block db is channel 32db + 8(r/4) + 4half + r%4
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (active) {
+    const float inv = 1.f / l_tot;
+    float* orow = p.out + (((int64_t)b * p.M + qi) * p.Hq + hq) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 v = {o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv, o[db][4 * r4 + 2] * inv,
+                          o[db][4 * r4 + 3] * inv};
+        *reinterpret_cast<float4*>(orow + 32 * db + 8 * r4 + 4 * half) = v;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_extend(const ExtendParams& p, int ng, int c, hipStream_t stream) {
+  const dim3 grid((unsigned)((int64_t)p.B * p.Hkv * p.row_blocks));
+  if (ng == 32 && c == 4)
+    hipLaunchKernelGGL((extend_kernel<32, 4>), grid, dim3(256), 0, stream, p);
+  else if (ng == 16 && c == 4)
+    hipLaunchKernelGGL((extend_kernel<16, 4>), grid, dim3(256), 0, stream, p);
+  else if (ng == 16 && c == 8)
+    hipLaunchKernelGGL((extend_kernel<16, 8>), grid, dim3(256), 0, stream, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace lvq

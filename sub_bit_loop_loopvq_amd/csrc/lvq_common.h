@@ -66,6 +66,31 @@ struct EncodeParams {
   unsigned long long* rerank_count;
 };
 
+struct ExtendParams {
+  int B, Hq, Hkv, P, R, G;
+  int M;                     // chunk rows per sequence (q, k_new, v_new, out stride)
+  int row_blocks;            // workgroups per (sequence, kv-head): ceil(M * Hq/Hkv / 128)
+  int pt_shift, max_pages, max_seq_len;
+  int tau;                   // loop step within its group (t mod G)
+  int64_t num_pages, page_bytes, kind_bytes, head_stride;
+  float scale_log2;          // softmax scale * log2(e)
+  const uint16_t* q;         // [B][M][Hq][d]
+  const uint16_t* k_new;     // [B][Hkv][M][d]
+  const uint16_t* v_new;
+  const int32_t* seq_lens;   // [B] cached tokens before the chunk
+  const int32_t* chunk_lens; // [B] or nullptr (all M)
+  const int32_t* block_table;
+  const uint8_t* pool_lj;    // pool + ((l*J + j)*Hkv) * head_stride, or nullptr (no VQ rows)
+  const uint16_t* cbk;       // prepared key codebooks of (l, jcb): [Hkv][G][K][d]
+  const uint16_t* cbv;
+  const uint16_t* k_prefix;  // [B][Hkv][P][d]
+  const uint16_t* v_prefix;
+  const uint16_t* k_recent;  // [B][Hkv][R][d]
+  const uint16_t* v_recent;
+  const float* rot;          // [d][d] or nullptr
+  float* out;                // [B][M][Hq][d]
+};
+
 struct PrepareParams {
   int64_t sets;              // L * Jcb * Hkv codebook sets
   int NG, K, c, G, d;
@@ -77,6 +102,7 @@ struct PrepareParams {
 // Launchers (defined next to their kernels).  Return hipSuccess or the launch error.
 hipError_t launch_decode(const DecodeParams& p, int ng, int c, hipStream_t stream);
 hipError_t launch_encode(const EncodeParams& p, int c, hipStream_t stream);
+hipError_t launch_extend(const ExtendParams& p, int ng, int c, hipStream_t stream);
 hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream);
 
 // ---------------------------------------------------------------------------

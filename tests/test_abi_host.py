@@ -38,6 +38,7 @@ def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(lvq.loopvq_encode_args) == 4 * 4 + 8 + 3 * 8 + 3 * 8 + 4 + 4 + 8 + 5 * 8
     assert ctypes.sizeof(lvq.loopvq_decode_args) == 6 * 4 + 8 + 10 * 8 + 8 + 8 + 8 + 8
     assert ctypes.sizeof(lvq.loopvq_evict_args) == 4 + 4 + 8 + 12 * 8
+    assert ctypes.sizeof(lvq.loopvq_extend_args) == 6 * 4 + 8 + 14 * 8 + 8 + 8
 
 
 @pytest.mark.parametrize("wl", W.ALL, ids=[w.name for w in W.ALL])
@@ -219,6 +220,31 @@ def test_evict_needs_a_recent_window_and_a_built_variant():
     with pytest.raises(lvq.LoopVQError) as e:
         lvq.loopvq_evict(cfg, **_evict_kw())
     assert e.value.status == lvq.LOOPVQ_ERR_UNSUPPORTED
+
+
+def _extend_kw(**over):
+    kw = dict(layer=0, loop=0, batch=2, chunk=16, q=FAKE, k_new=FAKE, v_new=FAKE, seq_lens=FAKE, max_seq_len=500,
+              out=FAKE, block_table=FAKE, pool=FAKE, max_pages_per_seq=8, num_pages=16, cb_k_prep=FAKE,
+              cb_v_prep=FAKE, k_prefix=FAKE, v_prefix=FAKE, k_recent=FAKE, v_recent=FAKE, stream=0)
+    kw.update(over)
+    return kw
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(chunk=0), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(loop=4), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(k_new=None), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(pool=None), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(k_recent=None), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(q=FAKE + 8), lvq.LOOPVQ_ERR_MISALIGNED),
+    (dict(out=FAKE + 4), lvq.LOOPVQ_ERR_MISALIGNED),
+    (dict(v_new=FAKE + 2), lvq.LOOPVQ_ERR_MISALIGNED),
+])
+def test_extend_rejects_before_launch(over, status):
+    cfg = lvq.make_config(W.LAYER_4K)
+    with pytest.raises(lvq.LoopVQError) as e:
+        lvq.loopvq_extend_attn(cfg, **_extend_kw(**over))
+    assert e.value.status == status
 
 
 def test_codebook_prepare_rejects():
