@@ -363,6 +363,154 @@ def encode_main(args):
     print(json.dumps(rec), flush=True)
 
 
+EXTEND_METRIC = "LoopVQ extend (chunked prefill) attention TFLOP/s over the packed cache"
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+class ExtendBench:
+    """Chunked prefill of M new tokens per sequence over a full packed cache of N tokens, one (layer, loop)."""
+
+    def __init__(self, wl, chunk, seed=0):
+        import torch
+        import sub_bit_loop_loopvq_amd as lvq
+        from synth import gen
+        from synth.device import DeviceGen
+        self.torch, self.lvq, self.wl, self.M = torch, lvq, wl, chunk
+        dev = "cuda"
+        B, H, Hq, d, P, R, T = wl.batch, wl.kv_heads, wl.q_heads, wl.head_dim, wl.prefix, wl.recent, wl.loops
+        self.cfg = lvq.make_config(wl)
+        self.pps = -(-wl.n_vq // wl.page_tokens)
+        self.num_pages = B * self.pps
+        lay = lvq.loopvq_layout_query(self.cfg, B, self.num_pages)
+        perm = np.random.default_rng(seed).permutation(self.num_pages).astype(np.int32)
+        self.bt = torch.from_numpy(perm.reshape(B, self.pps)).to(dev)
+        self.lens = torch.full((B,), wl.context, dtype=torch.int32, device=dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        # one (layer, loop group) slice of uniformly random 8-bit indices; the library addresses it from the pool base
+        slice_bytes = H * lay.pool_head_stride_bytes
+        self.pool = torch.randint(0, 256, (slice_bytes,), dtype=torch.uint8, device=dev, generator=g)
+        sc = gen.scales(wl)
+        self.prep = []
+        for kind in (0, 1):
+            cb = torch.from_numpy(gen.codebooks(wl, kind, sc, layers=[0]).view(np.int16)).to(dev)
+            prep = torch.empty_like(cb)
+            lvq.loopvq_codebook_prepare(self.cfg, cb, prep, None)
+            self.prep.append(prep)
+        dg = DeviceGen(wl)
+        self.win = []
+        for kind in (0, 1):
+            pre = torch.empty((B, H, P, d), dtype=torch.int16, device=dev)
+            rec = torch.empty((B, H, R, d), dtype=torch.int16, device=dev)
+            dg.kv(pre, kind=kind, layer=0, b0=0, nb=B, h0=0, nh=H, n0=0, nn=P, t0=0, nt=1, s_loop=0, s_b=H * P * d,
+                  s_h=P * d, s_n=d)
+            dg.kv(rec, kind=kind, layer=0, b0=0, nb=B, h0=0, nh=H, n0=wl.context - R, nn=R, t0=0, nt=1, s_loop=0,
+                  s_b=H * R * d, s_h=R * d, s_n=d)
+            self.win += [pre, rec]
+        # the chunk: the next M tokens of every sequence (generator positions past the cache)
+        self.kn = torch.empty((B, H, chunk, d), dtype=torch.int16, device=dev)
+        self.vn = torch.empty((B, H, chunk, d), dtype=torch.int16, device=dev)
+        for kind, buf in ((0, self.kn), (1, self.vn)):
+            dg.kv(buf, kind=kind, layer=0, b0=0, nb=B, h0=0, nh=H, n0=0, nn=chunk, t0=0, nt=1, s_loop=0,
+                  s_b=H * chunk * d, s_h=chunk * d, s_n=d)
+        self.q = (torch.randn((B, chunk, Hq, d), device=dev, generator=g)).to(torch.bfloat16).view(torch.int16)
+        self.out = torch.empty((B, chunk, Hq, d), dtype=torch.float32, device=dev)
+        self.rot = torch.from_numpy(gen.rotation_matrix_f32(wl)).to(dev) if wl.rotate_keys else None
+        torch.cuda.synchronize()
+
+    def run(self):
+        wl = self.wl
+        self.lvq.loopvq_extend_attn(self.cfg, layer=0, loop=0, batch=wl.batch, chunk=self.M, q=self.q, k_new=self.kn,
+                                    v_new=self.vn, seq_lens=self.lens, max_seq_len=wl.context, out=self.out,
+                                    block_table=self.bt, pool=self.pool, max_pages_per_seq=self.pps,
+                                    num_pages=self.num_pages, cb_k_prep=self.prep[0], cb_v_prep=self.prep[1],
+                                    k_prefix=self.win[0], v_prefix=self.win[2], k_recent=self.win[1],
+                                    v_recent=self.win[3], rot=self.rot)
+
+    def flops(self):
+        """Algorithmic flops of one launch: 2 per multiply-add of q.k and of p.v over every visible key."""
+        wl, M = self.wl, self.M
+        visible = M * wl.context + M * (M + 1) // 2
+        return 4.0 * wl.head_dim * wl.batch * wl.q_heads * visible
+
+
+def extend_cpu_baseline(wl, chunk, seconds: float) -> dict:
+    """The CPU oracle's extend attention (fp64, single BLAS thread) on sampled chunk rows of the workload."""
+    from threadpoolctl import threadpool_limits
+    from oracle import loopvq_oracle as O
+    from synth import gen
+    t_start = time.time()
+    sc = gen.scales(wl)
+    cbk = gen.bf16_to_f64(gen.codebooks(wl, 0, sc, layers=[0])[0, 0])
+    cbv = gen.bf16_to_f64(gen.codebooks(wl, 1, sc, layers=[0])[0, 0])
+    n_pre, n_vq, n_rec = O.split_context(wl.context, wl.prefix, wl.recent)
+    rng = np.random.default_rng(0)
+    rows, busy = 0, 0.0
+    with threadpool_limits(limits=1):
+        for b in range(wl.batch):
+            h = b % wl.kv_heads
+            win = [gen.bf16_to_f64(gen.kv_tokens(wl, kind, 0, b, h, n0, n1, 0, 1, sc)[:, 0])
+                   for kind in (0, 1) for (n0, n1) in ((0, n_pre), (wl.context - n_rec, wl.context))]
+            ik = gen.random_indices(wl, 0, 0, 0, b, h, n_vq)
+            iv = gen.random_indices(wl, 1, 0, 0, b, h, n_vq)
+            kc = gen.bf16_to_f64(gen.to_bf16_bits(rng.normal(size=(chunk, wl.head_dim))))
+            vc = gen.bf16_to_f64(gen.to_bf16_bits(rng.normal(size=(chunk, wl.head_dim))))
+            q = gen.bf16_to_f64(gen.to_bf16_bits(rng.normal(size=(8, wl.head_dim))))
+            c0 = time.perf_counter()
+            for i in range(8):     # rows chunk-8 .. chunk-1 of the chunk (the longest)
+                O.decode_query(q[i], win[0], win[2], ik, iv, cbk[h], cbv[h], np.concatenate([win[1], kc[:chunk - 7 + i]]),
+                               np.concatenate([win[3], vc[:chunk - 7 + i]]), 0, wl.chans, 1 / np.sqrt(wl.head_dim))
+            busy += time.perf_counter() - c0
+            rows += 8
+            if busy >= seconds:
+                break
+    vis = wl.context + chunk
+    return {"value": rows * 4.0 * wl.head_dim * vis / busy / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{rows} chunk rows (the last 8 of a {chunk}-row chunk, sequences 0..{rows // 8 - 1}) over "
+                       f"the full {wl.context}-token cache: unpack + dequantize + fp64 softmax attention, "
+                       f"{busy:.1f}s of timed oracle work, 1 BLAS thread; input setup untimed "
+                       f"(wall {time.time() - t_start:.1f}s)")}
+
+
+def extend_main(args):
+    import torch
+    from synth import workloads as W
+    wl = W.BY_NAME[args.workload]
+    torch.cuda.set_device(0)
+    eb = ExtendBench(wl, args.chunk)
+    for _ in range(args.warmup):
+        eb.run()
+    events = []
+    E = torch.cuda.Event
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        e0, e1 = E(enable_timing=True), E(enable_timing=True)
+        e0.record()
+        eb.run()
+        e1.record()
+        events.append((e0, e1))
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in events])
+    avg = float(us.mean())
+    tflops = eb.flops() / (avg * 1e-6) / 1e12
+    rec = {
+        "metric": EXTEND_METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": avg * 1e-3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "layers_timed": 1, "batch": wl.batch, "q_heads": wl.q_heads,
+                   "kv_heads": wl.kv_heads, "head_dim": wl.head_dim, "cached_tokens": wl.context,
+                   "chunk": args.chunk, "bits_per_elem": wl.index_bits / (wl.chans * wl.loop_group)},
+        "chunk_tokens_per_s": wl.batch * args.chunk / (avg * 1e-6),
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+        "launch_us": {"mean": avg, "p10": float(np.percentile(us, 10)), "p50": float(np.percentile(us, 50)),
+                      "p90": float(np.percentile(us, 90))},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = extend_cpu_baseline(wl, args.chunk, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
 def copy_calibration(nbytes: int, reps: int) -> None:
     """A plain device copy of known size, for scaling HBM counters (rocprofv3 --pmc)."""
     import torch
@@ -380,13 +528,18 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--workload", default=None,
+                    help="workload name (default: the 32K decode stack; --encode and --extend have their own)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, help="bytes; run only a plain copy (counter scaling)")
     ap.add_argument("--encode", action="store_true",
                     help="time the bulk encode of one (layer, loop group, kind) slice instead of the decode step "
                          "(default workload for this mode: deep4x32_h32_d128_b16_n8k)")
+    ap.add_argument("--extend", action="store_true",
+                    help="time extend (chunked prefill) attention over a packed cache instead of the decode step "
+                         "(default workload for this mode: layer16h_d128_b32_n4k)")
+    ap.add_argument("--chunk", type=int, default=512, help="chunk rows per sequence for --extend")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -394,11 +547,15 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 5)
         return
+    if args.extend:
+        args.workload = args.workload or "layer16h_d128_b32_n4k"
+        extend_main(args)
+        return
     if args.encode:
-        if args.workload == DEFAULT_WORKLOAD:
-            args.workload = "deep4x32_h32_d128_b16_n8k"
+        args.workload = args.workload or "deep4x32_h32_d128_b16_n8k"
         encode_main(args)
         return
+    args.workload = args.workload or DEFAULT_WORKLOAD
     import torch
     from synth import workloads as W
     wl = W.BY_NAME[args.workload]

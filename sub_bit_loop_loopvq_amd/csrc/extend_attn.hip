@@ -47,8 +47,8 @@ __device__ __forceinline__ void split2(float v, uint32_t& hi, uint32_t& lo) {
   lo = bf16_rne(v - __uint_as_float(hi << 16));
 }
 
-template <int NG, int C>
-__global__ void __launch_bounds__(256) extend_kernel(ExtendParams p) {
+template <int NG, int C, bool ROT>
+__global__ void __launch_bounds__(256, 2) extend_kernel(ExtendParams p) {
   constexpr int D = NG * C;
   constexpr int KROW = D + 8;         // bf16 per K row (16 B of padding)
   constexpr int KSTEPS = D / 16;      // k-steps of S^T = K Q^T
@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(256) extend_kernel(ExtendParams p) {
   const bool active = qi < Mb;
   const uint16_t* qrow = p.q + (((int64_t)b * p.M + (active ? qi : 0)) * p.Hq + hq) * D;
   u32x4 bq[KSTEPS], bq_lo[KSTEPS];
-  if (p.rot) {
+  if constexpr (ROT) {
     // q' = R^T q in fp32 for the 8 channels 16kk + 8*half + j this lane supplies, split in two
 #pragma unroll 1
     for (int kk = 0; kk < KSTEPS; ++kk) {
@@ -124,65 +124,134 @@ __global__ void __launch_bounds__(256) extend_kernel(ExtendParams p) {
   const uint16_t* slice_k = p.cbk ? p.cbk + ((int64_t)h * p.G + p.tau) * kCodes * D : nullptr;
   const uint16_t* slice_v = p.cbv ? p.cbv + ((int64_t)h * p.G + p.tau) * kCodes * D : nullptr;
 
-  // ---- staging -----------------------------------------------------------------------------
-  // bf16 rows: token t of the tile is row r0 + t of a [rows][D] window (t < count), else zeros
-  auto stage_rows = [&](const uint16_t* kw, const uint16_t* vw, int count) {
-    constexpr int PIECES = D / 8;                 // 16-byte pieces per row
-    for (int it = tid; it < kKT * PIECES; it += 256) {
-      const int t = it / PIECES, pc = it % PIECES;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (t < count) {
-        kv = *reinterpret_cast<const u32x4*>(kw + (int64_t)t * D + 8 * pc);
-        vv = *reinterpret_cast<const u32x4*>(vw + (int64_t)t * D + 8 * pc);
-      }
-      *reinterpret_cast<u32x4*>(ks + t * KROW + 8 * pc) = kv;
+  // ---- key tiles -----------------------------------------------------------------------------
+  // Tile k of this workgroup: prefix tiles, vector-quantized tiles, recent tiles, then the
+  // chunk's tiles up to the workgroup's last row.  A tile's packed indices are fetched while the
+  // previous tile is consumed; its keys are then gathered, written to LDS and consumed.  (Two
+  // workgroups share a CU, so one's staging overlaps the other's products.)
+  const int t_pre = (n_prefix + kKT - 1) / kKT, t_vq = (n_vq + kKT - 1) / kKT, t_rec = (n_recent + kKT - 1) / kKT;
+  const int t_ch = i_last / kKT + 1;
+  const int n_tiles = t_pre + t_vq + t_rec + t_ch;
+  struct Tile {
+    int seg, start, count;    // seg 0 prefix, 1 vector-quantized, 2 recent, 3 chunk
+  };
+  auto tile_of = [&](int k) -> Tile {
+    if (k < t_pre) return {0, k * kKT, n_prefix - k * kKT};
+    k -= t_pre;
+    if (k < t_vq) return {1, k * kKT, n_vq - k * kKT};
+    k -= t_vq;
+    if (k < t_rec) return {2, k * kKT, n_recent - k * kKT};
+    k -= t_rec;
+    return {3, k * kKT, i_last + 1 - k * kKT};
+  };
+  const uint16_t* k_seg[4] = {p.k_prefix + bhk * p.P * D, nullptr, p.k_recent + bhk * p.R * D, p.k_new + bhk * p.M * D};
+  const uint16_t* v_seg[4] = {p.v_prefix + bhk * p.P * D, nullptr, p.v_recent + bhk * p.R * D, p.v_new + bhk * p.M * D};
+
+  constexpr int PIECES = D / 8;                     // 16-byte pieces per bf16 row
+  constexpr int RITEMS = kKT * PIECES / 256;        // row pieces per thread
+  constexpr int QITEMS = kKT * (NG / 4) / 256;      // (token, group quad) items per thread
+  static_assert(RITEMS >= 1 && QITEMS >= 1, "tile mapping");
+  constexpr int FB = RITEMS * 4 > QITEMS * 4 * (C / 2) ? RITEMS * 4 : QITEMS * 4 * (C / 2);   // dwords per kind
+  uint32_t fk[FB], fv[FB];          // the tile's keys / values on their way to LDS
+  uint32_t ik_n[QITEMS], iv_n[QITEMS];   // packed indices of the next tile
+  bool ok_n[QITEMS];
+
+  // packed indices of a vector-quantized tile (token quads x group quads of one page: the tile
+  // is 64 aligned positions and a page holds a power of two >= 64, so one page per tile).  All
+  // loads are unconditional at clamped addresses; ok[] marks the real entries.
+  auto fetch_idx = [&](int k, uint32_t* ik, uint32_t* iv, bool* ok) {
+    const Tile tl = tile_of(k);
+    if (tl.seg != 1) return;
+    int page = p.block_table[(int64_t)b * p.max_pages + (tl.start >> p.pt_shift)];
+    const bool pok = page >= 0 && page < p.num_pages;
+    page = pok ? page : 0;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        vt[(8 * pc + 2 * w) * kVRow + t] = (uint16_t)(vv[w] & 0xffffu);
-        vt[(8 * pc + 2 * w + 1) * kVRow + t] = (uint16_t)(vv[w] >> 16);
-      }
+    for (int m = 0; m < QITEMS; ++m) {
+      const int it = tid + 256 * m;
+      const int t = it % kKT, gq = it / kKT;
+      ok[m] = pok && t < tl.count;
+      const int w = (tl.start + min(t, tl.count - 1)) & pt_mask;
+      const uint8_t* tile = pool_h + (int64_t)page * p.page_bytes + (((w >> 2) * (NG / 4) + gq) * 16 + (w & 3) * 4);
+      ik[m] = *reinterpret_cast<const uint32_t*>(tile);
+      iv[m] = *reinterpret_cast<const uint32_t*>(tile + p.kind_bytes);
     }
   };
-  // vector-quantized tokens u0 .. u0 + 63 (u < n_vq), dequantized from the loop-step slices
-  auto stage_vq = [&](int u0) {
-    for (int it = tid; it < kKT * (NG / 4); it += 256) {
-      const int t = it % kKT, gq = it / kKT;     // token, group quad
-      const int u = u0 + t;
-      uint32_t ik = 0u, iv = 0u;
-      bool ok = u < n_vq;
-      if (ok) {
-        int page = p.block_table[(int64_t)b * p.max_pages + (u >> p.pt_shift)];
-        ok = page >= 0 && page < p.num_pages;
-        if (ok) {
-          const int w = u & pt_mask;
-          const uint8_t* tile = pool_h + (int64_t)page * p.page_bytes + (((w >> 2) * (NG / 4) + gq) * 16 + (w & 3) * 4);
-          ik = *reinterpret_cast<const uint32_t*>(tile);
-          iv = *reinterpret_cast<const uint32_t*>(tile + p.kind_bytes);
-        }
-      }
+  bool ok_cur[QITEMS];   // ok flags of the tile whose keys are in fk / fv
+  // keys / values of tile k into registers (vector-quantized rows from their indices); rows past
+  // the tile's count read the last valid row and are zeroed by store()
+  auto fetch = [&](int k, const uint32_t* ik, const uint32_t* iv, const bool* ok) {
+    const Tile tl = tile_of(k);
+    if (tl.seg == 1) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int g = 4 * gq + r;
-        const uint32_t kx = (ik >> (8 * r)) & 0xffu, vx = (iv >> (8 * r)) & 0xffu;
-        uint32_t kw[C / 2], vw[C / 2];
-        if (ok) {
+      for (int m = 0; m < QITEMS; ++m) {
+        ok_cur[m] = ok[m];
+        const int gq = (tid + 256 * m) / kKT;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int g = 4 * gq + r;
+          const uint32_t kx = (ik[m] >> (8 * r)) & 0xffu, vx = (iv[m] >> (8 * r)) & 0xffu;
           const uint32_t* kc = reinterpret_cast<const uint32_t*>(slice_k + kx * D + g * C);
           const uint32_t* vc = reinterpret_cast<const uint32_t*>(slice_v + vx * D + g * C);
 #pragma unroll
           for (int e = 0; e < C / 2; ++e) {
-            kw[e] = kc[e];
-            vw[e] = vc[e];
+            fk[(m * 4 + r) * (C / 2) + e] = kc[e];
+            fv[(m * 4 + r) * (C / 2) + e] = vc[e];
           }
-        } else {
-#pragma unroll
-          for (int e = 0; e < C / 2; ++e) kw[e] = vw[e] = 0u;
         }
-        uint32_t* kd = reinterpret_cast<uint32_t*>(ks + t * KROW + g * C);
+      }
+    } else {
+      const uint16_t* kw = (tl.seg == 0 ? k_seg[0] : tl.seg == 2 ? k_seg[2] : k_seg[3]) + (int64_t)tl.start * D;
+      const uint16_t* vw = (tl.seg == 0 ? v_seg[0] : tl.seg == 2 ? v_seg[2] : v_seg[3]) + (int64_t)tl.start * D;
 #pragma unroll
-        for (int e = 0; e < C / 2; ++e) {
-          kd[e] = kw[e];
-          vt[(g * C + 2 * e) * kVRow + t] = (uint16_t)(vw[e] & 0xffffu);
-          vt[(g * C + 2 * e + 1) * kVRow + t] = (uint16_t)(vw[e] >> 16);
+      for (int m = 0; m < RITEMS; ++m) {
+        const int it = tid + 256 * m;
+        const int t = min(it / PIECES, tl.count - 1), pc = it % PIECES;
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(kw + (int64_t)t * D + 8 * pc);
+        const u32x4 vv = *reinterpret_cast<const u32x4*>(vw + (int64_t)t * D + 8 * pc);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          fk[4 * m + w] = kv[w];
+          fv[4 * m + w] = vv[w];
+        }
+      }
+    }
+  };
+  // the registers of tile k into LDS: K as [token][d], V transposed [d][token]; entries past the
+  // tile's keys are written as zeros
+  auto store = [&](int k) {
+    const Tile tl = tile_of(k);
+    if (tl.seg == 1) {
+#pragma unroll
+      for (int m = 0; m < QITEMS; ++m) {
+        const int it = tid + 256 * m;
+        const int t = it % kKT, gq = it / kKT;
+        const uint32_t keep = ok_cur[m] ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int g = 4 * gq + r;
+          uint32_t* kd = reinterpret_cast<uint32_t*>(ks + t * KROW + g * C);
+#pragma unroll
+          for (int e = 0; e < C / 2; ++e) {
+            const uint32_t vw = fv[(m * 4 + r) * (C / 2) + e] & keep;
+            kd[e] = fk[(m * 4 + r) * (C / 2) + e] & keep;
+            vt[(g * C + 2 * e) * kVRow + t] = (uint16_t)(vw & 0xffffu);
+            vt[(g * C + 2 * e + 1) * kVRow + t] = (uint16_t)(vw >> 16);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < RITEMS; ++m) {
+        const int it = tid + 256 * m;
+        const int t = it / PIECES, pc = it % PIECES;
+        const uint32_t keep = t < tl.count ? 0xffffffffu : 0u;
+        *reinterpret_cast<u32x4*>(ks + t * KROW + 8 * pc) =
+            u32x4{fk[4 * m] & keep, fk[4 * m + 1] & keep, fk[4 * m + 2] & keep, fk[4 * m + 3] & keep};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t vw = fv[4 * m + w] & keep;
+          vt[(8 * pc + 2 * w) * kVRow + t] = (uint16_t)(vw & 0xffffu);
+          vt[(8 * pc + 2 * w + 1) * kVRow + t] = (uint16_t)(vw >> 16);
         }
       }
     }
@@ -194,13 +263,18 @@ __global__ void __launch_bounds__(256) extend_kernel(ExtendParams p) {
     f32x16 s[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      f32x16 acc = {};
+      // all of the block's K operands first, so the LDS reads overlap instead of each MFMA
+      // waiting for its own
+      u32x4 a[KSTEPS];
       const uint16_t* krow = ks + (32 * mb + col) * KROW + 8 * half;
 #pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) a[kk] = *reinterpret_cast<const u32x4*>(krow + 16 * kk);
+      f32x16 acc = {};
+#pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + 16 * kk);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bq[kk]), acc, 0, 0, 0);
-        if (p.rot) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bq_lo[kk]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[kk]), as_bf16x8(bq[kk]), acc, 0, 0, 0);
+        if constexpr (ROT)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[kk]), as_bf16x8(bq_lo[kk]), acc, 0, 0, 0);
       }
       s[mb] = acc;
     }
@@ -248,48 +322,32 @@ __global__ void __launch_bounds__(256) extend_kernel(ExtendParams p) {
       for (int j = 0; j < 8; ++j) split2(s[mb][r0 + j], hi[j], lo[j]);
       const u32x4 bh = {hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
       const u32x4 bl = {lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
+      u32x4 a[DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const uint16_t* vrow = vt + (32 * db + col) * kVRow + 16 * kst + 4 * half;
         const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
         const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 8);
-        const u32x4 a = {v0.x, v0.y, v1.x, v1.y};
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bh), o[db], 0, 0, 0);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bl), o[db], 0, 0, 0);
+        a[db] = u32x4{v0.x, v0.y, v1.x, v1.y};
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[db]), as_bf16x8(bh), o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[db]), as_bf16x8(bl), o[db], 0, 0, 0);
       }
     }
   };
 
-  // ---- the key segments: prefix, vector-quantized, recent, the chunk itself (causal) ----------
-  const uint16_t* kp = p.k_prefix + bhk * p.P * D;
-  const uint16_t* vp = p.v_prefix + bhk * p.P * D;
-  for (int t0 = 0; t0 < n_prefix; t0 += kKT) {
+  // ---- the key tiles ------------------------------------------------------------------------------
+  fetch_idx(0, ik_n, iv_n, ok_n);
+  for (int k = 0; k < n_tiles; ++k) {
+    fetch(k, ik_n, iv_n, ok_n);
+    if (k + 1 < n_tiles) fetch_idx(k + 1, ik_n, iv_n, ok_n);
+    __syncthreads();                  // every wave is done with the previous tile
+    store(k);
     __syncthreads();
-    stage_rows(kp + (int64_t)t0 * D, vp + (int64_t)t0 * D, n_prefix - t0);
-    __syncthreads();
-    consume(n_prefix - t0, -1);
-  }
-  for (int u0 = 0; u0 < n_vq; u0 += kKT) {
-    __syncthreads();
-    stage_vq(u0);
-    __syncthreads();
-    consume(n_vq - u0, -1);
-  }
-  const uint16_t* kr = p.k_recent + bhk * p.R * D;
-  const uint16_t* vr = p.v_recent + bhk * p.R * D;
-  for (int t0 = 0; t0 < n_recent; t0 += kKT) {
-    __syncthreads();
-    stage_rows(kr + (int64_t)t0 * D, vr + (int64_t)t0 * D, n_recent - t0);
-    __syncthreads();
-    consume(n_recent - t0, -1);
-  }
-  const uint16_t* kc = p.k_new + bhk * p.M * D;
-  const uint16_t* vc = p.v_new + bhk * p.M * D;
-  for (int j0 = 0; j0 <= i_last; j0 += kKT) {
-    __syncthreads();
-    stage_rows(kc + (int64_t)j0 * D, vc + (int64_t)j0 * D, i_last + 1 - j0);
-    __syncthreads();
-    consume(i_last + 1 - j0, j0);
+    const Tile tl = tile_of(k);
+    consume(tl.count, tl.seg == 3 ? tl.start : -1);
   }
 
   // ---- normalise and write: O^T register r of block db is channel 32db + 8(r/4) + 4half + r%4
@@ -310,17 +368,21 @@ __global__ void __launch_bounds__(256) extend_kernel(ExtendParams p) {
 
 }  // namespace
 
-hipError_t launch_extend(const ExtendParams& p, int ng, int c, hipStream_t stream) {
+template <int NG, int C>
+hipError_t launch_extend_variant(const ExtendParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.B * p.Hkv * p.row_blocks));
-  if (ng == 32 && c == 4)
-    hipLaunchKernelGGL((extend_kernel<32, 4>), grid, dim3(256), 0, stream, p);
-  else if (ng == 16 && c == 4)
-    hipLaunchKernelGGL((extend_kernel<16, 4>), grid, dim3(256), 0, stream, p);
-  else if (ng == 16 && c == 8)
-    hipLaunchKernelGGL((extend_kernel<16, 8>), grid, dim3(256), 0, stream, p);
+  if (p.rot)
+    hipLaunchKernelGGL((extend_kernel<NG, C, true>), grid, dim3(256), 0, stream, p);
   else
-    return hipErrorInvalidValue;
+    hipLaunchKernelGGL((extend_kernel<NG, C, false>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+hipError_t launch_extend(const ExtendParams& p, int ng, int c, hipStream_t stream) {
+  if (ng == 32 && c == 4) return launch_extend_variant<32, 4>(p, stream);
+  if (ng == 16 && c == 4) return launch_extend_variant<16, 4>(p, stream);
+  if (ng == 16 && c == 8) return launch_extend_variant<16, 8>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace lvq
