@@ -30,7 +30,11 @@ Readings where the pages are silent (each one is listed in the design notes)
 * context split: tokens [0, P) prefix, [P, N - R) vector-quantized, the rest
   recent; N includes the token being decoded; no mask inside the cache;
 * softmax scale 1/sqrt(d) unless given; a key rotation R is undone by q' = R^T q;
-* packed layout: see ``page_layout`` below.
+* packed layout: see ``page_layout`` below;
+* codebook learning ([AIR] opening summary, Fisher-weighted k-means): one scalar
+  weight per sample (sub-vector) stands in for the Fisher weight, the assignment is
+  the encode rule, a codeword that receives no weight keeps its value, and the new
+  codeword is the weighted mean rounded to bf16 (the codebook's storage type).
 
 Pins that tie this file to something other than itself live in
 ``tests/test_oracle_pins.py`` (brute force, scipy, closed forms, hand-worked
@@ -297,6 +301,49 @@ def extend_attention(q_rows, k_prefix, v_prefix, idx_k, idx_v, cb_k, cb_v, k_rec
         o[i], lse[i] = decode_query(q_rows[i], k_prefix, v_prefix, idx_k, idx_v, cb_k, cb_v, kr, vr, tau, c,
                                     scale, rot)
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Codebook learning: weighted Lloyd iterations
+# ---------------------------------------------------------------------------
+def round_to_bf16(v: np.ndarray) -> np.ndarray:
+    """fp64 -> nearest bf16 value (8 significant bits, ties to even), returned as fp64.
+
+    Written out from the definition: v = m * 2**e with 0.5 <= |m| < 1, so the nearest
+    bf16 is round_half_even(m * 2**8) * 2**(e - 8).  (Normal range only.)
+    """
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)
+    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
+
+
+def lloyd_step(x: np.ndarray, w: np.ndarray, C: np.ndarray, to_bf16: bool = True):
+    """One Fisher-weighted Lloyd iteration for one codebook ([AIR] opening summary: the codebook
+    comes from k-means weighted by Fisher information, before the output-matching fine-tune,
+    which is not part of this path).
+
+    x [n][E] sub-vectors, w [n] non-negative weights (the Fisher weights; synthetic here),
+    C [K][E] current codebook.  Assignment: the encode rule (nearest, lowest index on ties).
+    Update: each codeword that received weight becomes the weighted mean of its sub-vectors,
+    sum_n w_n x_n / sum_n w_n; a codeword with no weight keeps its value (reading: the pages
+    are silent on empty clusters).  Codebooks are stored in bf16, so the new codeword is the
+    mean rounded to bf16 (to_bf16=False keeps fp64, for the pins).
+    Returns (assign [n], C_new [K][E], distortion), distortion = sum_n w_n ||x_n - C[a_n]||^2
+    against the codebook the assignment used.
+    """
+    K, E = C.shape
+    a, d1, _ = encode(x, C)
+    distortion = float(np.sum(w * d1))
+    wsum = np.zeros(K)
+    sums = np.zeros((K, E))
+    for n in range(x.shape[0]):            # plain accumulation, row order
+        wsum[a[n]] += w[n]
+        sums[a[n]] += w[n] * x[n]
+    C_new = C.astype(np.float64).copy()
+    hit = wsum > 0
+    mean = sums[hit] / wsum[hit][:, None]
+    C_new[hit] = round_to_bf16(mean) if to_bf16 else mean
+    return a, C_new, distortion
 
 
 def near_tie(d1: np.ndarray, d2: np.ndarray, rel: float = 1e-6) -> np.ndarray:

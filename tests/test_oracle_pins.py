@@ -455,3 +455,63 @@ def test_extend_closed_forms():
         vis = np.concatenate([base, f["vc"][:i + 1]])
         assert np.allclose(o[i], vis.mean(axis=0), rtol=1e-13, atol=1e-14)
         assert lse[i] == pytest.approx(np.log(len(vis)), rel=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Weighted Lloyd iteration (codebook learning)
+# ---------------------------------------------------------------------------
+def test_round_to_bf16_matches_the_bit_level_rounding():
+    r = _rng(30)
+    v = np.concatenate([r.normal(size=2000) * 10.0 ** r.integers(-8, 8, 2000), [1.0, 1.00390625, 1.01171875, -3.5]])
+    # bit level: fp64 -> fp32 is exact for these (they are made exact in fp32 first), then the
+    # bf16 round-half-even on the fp32 bits
+    v32 = v.astype(np.float32).astype(np.float64)
+    u = v32.astype(np.float32).view(np.uint32).astype(np.uint64)
+    bits = ((u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)).astype(np.uint32)
+    ref = (bits << np.uint32(16)).view(np.float32).astype(np.float64)
+    assert np.array_equal(O.round_to_bf16(v32), ref)
+    # ties go to the even significand: 1 + 2^-8 sits halfway between 1 and 1 + 2^-7
+    assert O.round_to_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
+    assert O.round_to_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+
+
+def test_lloyd_hand_example():
+    x = np.array([[0.0], [1.0], [10.0], [11.0]])
+    w = np.array([1.0, 3.0, 1.0, 1.0])
+    C = np.array([[0.0], [10.0]])
+    a, C1, dist = O.lloyd_step(x, w, C)
+    assert list(a) == [0, 0, 1, 1]
+    assert np.array_equal(C1, np.array([[0.75], [10.5]]))
+    assert dist == pytest.approx(3.0 + 1.0)
+
+
+def test_lloyd_single_codeword_is_the_weighted_mean():
+    r = _rng(31)
+    x, w = r.normal(size=(500, 16)), r.uniform(0.1, 3.0, 500)
+    _, C1, _ = O.lloyd_step(x, w, np.zeros((1, 16)), to_bf16=False)
+    assert np.allclose(C1[0], np.average(x, axis=0, weights=w), rtol=1e-13, atol=1e-15)
+
+
+def test_lloyd_matches_sklearn_weighted_kmeans_iteration():
+    from sklearn.cluster import KMeans
+    r = _rng(32)
+    K, E = 12, 16
+    centers = r.normal(size=(K, E)) * 4
+    x = np.concatenate([centers[k] + r.normal(size=(40, E)) for k in range(K)])
+    w = r.uniform(0.2, 2.0, len(x))
+    C0 = centers + r.normal(size=(K, E)) * 0.5
+    _, C1, _ = O.lloyd_step(x, w, C0, to_bf16=False)
+    km = KMeans(n_clusters=K, init=C0, n_init=1, max_iter=1, algorithm="lloyd", tol=0.0).fit(x, sample_weight=w)
+    assert np.allclose(C1, km.cluster_centers_, rtol=1e-10, atol=1e-12)
+
+
+def test_lloyd_keeps_empty_codewords_and_decreases_the_objective():
+    r = _rng(33)
+    x, w = r.normal(size=(300, 8)), r.uniform(0.5, 1.5, 300)
+    C = np.concatenate([r.normal(size=(6, 8)), np.full((1, 8), 1e3)])   # the far codeword gets nothing
+    prev = np.inf
+    for _ in range(6):
+        a, C_new, dist = O.lloyd_step(x, w, C, to_bf16=False)
+        assert not (a == 6).any() and np.array_equal(C_new[6], C[6])
+        assert dist <= prev * (1 + 1e-12)
+        prev, C = dist, C_new
