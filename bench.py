@@ -511,6 +511,137 @@ def extend_main(args):
     print(json.dumps(rec), flush=True)
 
 
+LLOYD_METRIC = "LoopVQ weighted Lloyd iteration sub-vectors/s (one codebook set: assignment + weighted update)"
+
+
+class LloydBench:
+    """One weighted k-means iteration of one (layer, loop group, kind) codebook set over the encode
+    workload's tokens as samples: the assignment (the encode kernels without a pool), then the
+    weighted update (sums, weights, new codewords and norms)."""
+
+    def __init__(self, wl, layer=0, loop_group=0, kind=0):
+        import torch
+        import sub_bit_loop_loopvq_amd as lvq
+        from synth import gen
+        from synth.device import DeviceGen
+        self.torch, self.lvq, self.wl = torch, lvq, wl
+        self.layer, self.j = layer, loop_group
+        dev = "cuda"
+        B, H, d, G, P = wl.batch, wl.kv_heads, wl.head_dim, wl.loop_group, wl.prefix
+        self.n = n = wl.encode_tokens
+        per_seq = n // B
+        self.cfg = lvq.make_config(wl)
+        lay = lvq.loopvq_layout_query(self.cfg, 1, 1)
+        sc = gen.scales(wl)
+        self.cb = torch.from_numpy(gen.codebooks(wl, kind, sc, layers=[layer]).view(np.int16)).to(dev)
+        self.norms = torch.empty(lay.norms_elems, dtype=torch.float32, device=dev)
+        lvq.loopvq_codebook_prepare(self.cfg, self.cb, torch.empty_like(self.cb), self.norms)
+        self.src = torch.empty((G, n, H, d), dtype=torch.int16, device=dev)
+        dg = DeviceGen(wl)
+        for b in range(B):
+            dg.kv(self.src[:, b * per_seq:], kind=kind, layer=layer, b0=b, nb=1, h0=0, nh=H, n0=P, nn=per_seq,
+                  t0=loop_group * G, nt=G, s_loop=n * H * d, s_b=0, s_h=d, s_n=H * d)
+        self.w = torch.from_numpy(gen.sample_weights(wl, n)).to(dev)
+        self.assign = torch.empty((n, H, wl.groups), dtype=torch.int32, device=dev)
+        self.ws = torch.empty(lvq.loopvq_lloyd_workspace(self.cfg, n), dtype=torch.uint8, device=dev)
+        self.dist = torch.empty((H, wl.groups), dtype=torch.float64, device=dev)
+        self.strides = dict(stride_loop=n * H * d, stride_token=H * d, stride_head=d)
+        self.jc = loop_group if wl.codebook_per_loop_group else 0
+        torch.cuda.synchronize()
+
+    def step(self, e0=None, e1=None, e2=None):
+        wl, lvq = self.wl, self.lvq
+        if e0 is not None:
+            e0.record()
+        lvq.loopvq_encode(self.cfg, layer=self.layer, loop_group=self.j, kind=0, n_tokens=self.n, src=self.src,
+                          seq_id=None, vq_pos=None, block_table=None, batch=1, max_pages_per_seq=1, num_pages=1,
+                          cb=self.cb, cb_norms=self.norms, pool=None, out_idx=self.assign, **self.strides)
+        if e1 is not None:
+            e1.record()
+        lvq.loopvq_lloyd_update(self.cfg, layer=self.layer, cb_set=self.jc, n_samples=self.n, src=self.src,
+                                weight=self.w, cb=self.cb, cb_norms=self.norms, assign=self.assign,
+                                workspace=self.ws, distortion=self.dist, **self.strides)
+        if e2 is not None:
+            e2.record()
+
+
+def lloyd_cpu_baseline(wl, seconds: float, layer=0, loop_group=0, kind=0) -> dict:
+    """The oracle's Lloyd iteration (fp64 brute-force assignment + plain weighted accumulation, one BLAS
+    thread) on whole (kv-head, group) sample sets of the same workload."""
+    from threadpoolctl import threadpool_limits
+    from oracle import loopvq_oracle as O
+    from synth import gen
+    t_start = time.time()
+    sc = gen.scales(wl)
+    cb = gen.bf16_to_f64(gen.codebooks(wl, kind, sc, layers=[layer])[layer, 0])   # [H][NG][K][E]
+    per_seq = wl.encode_tokens // wl.batch
+    G, n = wl.loop_group, wl.encode_tokens
+    w = gen.sample_weights(wl, n)
+    planes = np.concatenate([gen.kv_tokens(wl, kind, layer, b, 0, wl.prefix, wl.prefix + per_seq, loop_group * G,
+                                           loop_group * G + G, sc) for b in range(wl.batch)])     # [n][G][d], head 0
+    x = O.subvectors(gen.bf16_to_f64(planes).transpose(1, 0, 2), wl.chans)                       # [n][NG][E]
+    done, busy, groups = 0, 0.0, 0
+    with threadpool_limits(limits=1):
+        for g in range(wl.groups):
+            c0 = time.perf_counter()
+            O.lloyd_step(x[:, g], w[:, 0, g].astype(np.float64), cb[0, g])
+            busy += time.perf_counter() - c0
+            done += n
+            groups += 1
+            if busy >= seconds:
+                break
+    return {"value": done / busy, "unit": "sub-vectors/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{groups} whole (kv-head 0, group) sample sets of {n} sub-vectors each of layer {layer}, "
+                       f"loop group {loop_group}, kind {kind}: one weighted Lloyd iteration each (fp64 brute-force "
+                       f"assignment over {wl.codewords} codewords, weighted means, bf16 rounding); {busy:.1f}s of "
+                       f"timed oracle work, 1 BLAS thread; input setup untimed (wall {time.time() - t_start:.1f}s)")}
+
+
+def lloyd_main(args):
+    import torch
+    from synth import workloads as W
+    wl = W.BY_NAME[args.workload]
+    torch.cuda.set_device(0)
+    lb = LloydBench(wl)
+    for _ in range(args.warmup):
+        lb.step()
+    E = torch.cuda.Event
+    ev = [(E(enable_timing=True), E(enable_timing=True), E(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        lb.step(*e)
+    torch.cuda.synchronize()
+    t_as = np.array([a.elapsed_time(b) * 1e3 for a, b, _ in ev])
+    t_up = np.array([b.elapsed_time(c) * 1e3 for _, b, c in ev])
+    t_st = np.array([a.elapsed_time(c) * 1e3 for a, _, c in ev])
+    subvec = wl.encode_tokens * wl.kv_heads * wl.groups
+    compares = subvec * wl.codewords
+    # update: every sample element read once, its index and weight once, the set's codebook read and written
+    up_bytes = subvec * (wl.sub_len * 2 + 4 + 4) + 2 * wl.kv_heads * wl.groups * wl.codewords * wl.sub_len * 2
+    a_us, u_us, s_us = float(t_as.mean()), float(t_up.mean()), float(t_st.mean())
+    rec = {
+        "metric": LLOYD_METRIC, "value": subvec / (s_us * 1e-6), "unit": "sub-vectors/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": s_us * 1e-3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "samples": wl.encode_tokens, "kv_heads": wl.kv_heads, "groups": wl.groups,
+                   "sub_len": wl.sub_len, "codewords": wl.codewords, "layer": 0, "loop_group": 0, "kind": "K",
+                   "weights": "seeded stand-ins for Fisher information, one per sample, 1 in 16 zero"},
+        "roofline": {"bound": "alu", "achieved": compares / (a_us * 1e-6) / 1e12, "peak": VALU_PEAK_OPS / 1e12,
+                     "unit": "Tcompare/s at one VALU op per compare", "frac": compares / (a_us * 1e-6) / VALU_PEAK_OPS,
+                     "traffic": None, "kernel": "assignment (encode kernels without a pool)"},
+        "update_roofline": {"bound": "hbm", "achieved": up_bytes / (u_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS,
+                            "unit": "GB/s", "frac": up_bytes / (u_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                            "traffic": None, "bytes": up_bytes},
+        "assign_us": a_us, "update_us": u_us,
+        "step_us": {"mean": s_us, "p10": float(np.percentile(t_st, 10)), "p50": float(np.percentile(t_st, 50)),
+                    "p90": float(np.percentile(t_st, 90))},
+        "distortion_sum_last": float(lb.dist.sum().item()),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = lloyd_cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
 def copy_calibration(nbytes: int, reps: int) -> None:
     """A plain device copy of known size, for scaling HBM counters (rocprofv3 --pmc)."""
     import torch
@@ -540,6 +671,9 @@ def main():
                     help="time extend (chunked prefill) attention over a packed cache instead of the decode step "
                          "(default workload for this mode: layer16h_d128_b32_n4k)")
     ap.add_argument("--chunk", type=int, default=512, help="chunk rows per sequence for --extend")
+    ap.add_argument("--lloyd", action="store_true",
+                    help="time one weighted Lloyd iteration of one codebook set instead of the decode step "
+                         "(default workload for this mode: deep4x32_h32_d128_b16_n8k)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -554,6 +688,10 @@ def main():
     if args.encode:
         args.workload = args.workload or "deep4x32_h32_d128_b16_n8k"
         encode_main(args)
+        return
+    if args.lloyd:
+        args.workload = args.workload or "deep4x32_h32_d128_b16_n8k"
+        lloyd_main(args)
         return
     args.workload = args.workload or DEFAULT_WORKLOAD
     import torch

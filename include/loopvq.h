@@ -150,7 +150,9 @@ typedef struct loopvq_encode_args {
   int64_t num_pages;            /* pages per (layer, loop group, kv-head) in the pool */
   const uint16_t* cb;           /* device canonical codebooks of this kind, bf16 */
   const float* cb_norms;        /* device squared norms of this kind (loopvq_codebook_prepare) */
-  uint8_t* pool;                /* device index pool (written) */
+  uint8_t* pool;                /* device index pool (written), or NULL for the assignment alone:
+                                   then seq_id, vq_pos, block_table, batch, max_pages_per_seq and
+                                   num_pages are not read and out_idx is required */
   int32_t* out_idx;             /* optional device [n_tokens][Hkv][NG] copy of the chosen indices */
   unsigned long long* rerank_count; /* optional device counter: += sub-vectors re-scored in fp64 */
 } loopvq_encode_args;
@@ -189,6 +191,62 @@ typedef struct loopvq_evict_args {
 } loopvq_evict_args;
 
 loopvq_status loopvq_evict(const loopvq_config* cfg, const loopvq_evict_args* args, void* stream);
+
+/* Lloyd step: one iteration of the weighted k-means that learns the codebooks
+ * (airadar.tv summary, opening summary: the codebooks come from k-means weighted
+ * by Fisher information).  For the codebook set (layer, cb_set) of one kind
+ * (cb_set = loop group j with codebook_per_loop_group, else 0), every kv-head h
+ * and channel group g:
+ *   1. assignment: a[r][h][g] = nearest codeword of sample r's sub-vector under
+ *      the current codebook, lowest index on ties, exactly as loopvq_encode picks
+ *      it (the sub-vector of row r is built from the G sample planes like an
+ *      encode row: element tau*c + i is channel g*c + i of plane tau);
+ *   2. update: codeword k becomes sum_r w[r][h][g] x_r / sum_r w[r][h][g] over the
+ *      samples assigned to it, rounded to the nearest bf16 (ties to even); a
+ *      codeword whose samples weigh nothing keeps its value.  The sums are fp64
+ *      in an unspecified order, so a mean within about 1e-12 (relative) of a
+ *      bf16 rounding midpoint may round either way;
+ *   3. the set's squared norms in cb_norms are recomputed as
+ *      loopvq_codebook_prepare computes them.  The decode-side prepared copy is
+ *      not touched: call loopvq_codebook_prepare after the last iteration.
+ * Samples: plane tau of row r, kv-head h at src + tau*stride_loop +
+ * r*stride_token + h*stride_head (elements), channels contiguous.  The weights
+ * stand in for the Fisher information: one per sample and group, finite and
+ * >= 0.  All of one call's work is on `stream`; nothing is allocated: the
+ * caller passes a workspace of at least loopvq_lloyd_workspace() bytes, which
+ * must not be shared by calls that may overlap. */
+typedef struct loopvq_lloyd_args {
+  int32_t layer;                /* l in [0, L) */
+  int32_t cb_set;               /* in [0, Jcb): the loop group with per-group codebooks, else 0 */
+  int32_t n_samples;            /* n >= 0 */
+  const uint16_t* src;          /* device bf16, 16-byte aligned */
+  int64_t stride_loop;          /* elements; all three multiples of 8 */
+  int64_t stride_token;
+  int64_t stride_head;
+  const float* weight;          /* device fp32 [n][Hkv][NG], 16-byte aligned */
+  uint16_t* cb;                 /* device canonical codebooks of one kind [L][Jcb][Hkv][NG][K][E]:
+                                   the set's codewords are updated in place */
+  float* cb_norms;              /* device squared norms of the same kind: the set's are rewritten */
+  int32_t* assign;              /* device [n][Hkv][NG], 16-byte aligned: written with step 1
+                                   (read by loopvq_lloyd_update) */
+  double* cluster_weight;       /* optional device [Hkv][NG][K]: total weight of each codeword */
+  double* distortion;           /* optional device [Hkv][NG]: sum_r w ||x_r - C[a_r]||^2 under the
+                                   codebook before the update */
+  void* workspace;              /* device, 16-byte aligned */
+  size_t workspace_bytes;
+  unsigned long long* rerank_count; /* optional device counter, as for loopvq_encode */
+} loopvq_lloyd_args;
+
+/* Workspace bytes loopvq_lloyd_step and loopvq_lloyd_update need for n_samples samples. */
+loopvq_status loopvq_lloyd_workspace(const loopvq_config* cfg, int32_t n_samples, size_t* bytes);
+
+/* Steps 1-3 above. */
+loopvq_status loopvq_lloyd_step(const loopvq_config* cfg, const loopvq_lloyd_args* args, void* stream);
+
+/* Steps 2-3 alone, with `assign` an input: the assignment of the same samples
+ * under the set's current codebook, e.g. loopvq_encode's out_idx (without a
+ * pool).  Same arguments and rules as loopvq_lloyd_step; rerank_count unused. */
+loopvq_status loopvq_lloyd_update(const loopvq_config* cfg, const loopvq_lloyd_args* args, void* stream);
 
 /* Decode attention for one (layer l, loop step t) over all B sequences and Hq
  * query heads: for query (b, hq) with kv-head h = hq / (Hq/Hkv) and N =

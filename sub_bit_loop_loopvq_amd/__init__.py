@@ -53,6 +53,13 @@ class loopvq_evict_args(ctypes.Structure):
                 ("norms_k", _P), ("norms_v", _P), ("pool", _P), ("out_idx", _P), ("rerank_count", _P)]
 
 
+class loopvq_lloyd_args(ctypes.Structure):
+    _fields_ = [("layer", _I32), ("cb_set", _I32), ("n_samples", _I32), ("src", _P), ("stride_loop", _I64),
+                ("stride_token", _I64), ("stride_head", _I64), ("weight", _P), ("cb", _P), ("cb_norms", _P),
+                ("assign", _P), ("cluster_weight", _P), ("distortion", _P), ("workspace", _P),
+                ("workspace_bytes", ctypes.c_size_t), ("rerank_count", _P)]
+
+
 class loopvq_decode_args(ctypes.Structure):
     _fields_ = [("layer", _I32), ("loop", _I32), ("batch", _I32), ("max_pages_per_seq", _I32),
                 ("max_seq_len", _I32), ("num_splits", _I32), ("num_pages", _I64),
@@ -71,7 +78,9 @@ class loopvq_extend_args(ctypes.Structure):
 
 
 EXPORTS = ("loopvq_config_check", "loopvq_bits_per_elem", "loopvq_layout_query", "loopvq_codebook_prepare",
-           "loopvq_encode", "loopvq_evict", "loopvq_decode_attn_workspace", "loopvq_decode_attn",
+           "loopvq_encode", "loopvq_evict", "loopvq_lloyd_workspace", "loopvq_lloyd_step",
+           "loopvq_lloyd_update",
+           "loopvq_decode_attn_workspace", "loopvq_decode_attn",
            "loopvq_extend_attn", "loopvq_status_string", "loopvq_last_error")
 
 _lib = None
@@ -95,6 +104,12 @@ def lib() -> ctypes.CDLL:
         L.loopvq_encode.restype = _I32
         L.loopvq_evict.argtypes = [cfgp, ctypes.POINTER(loopvq_evict_args), _P]
         L.loopvq_evict.restype = _I32
+        L.loopvq_lloyd_workspace.argtypes = [cfgp, _I32, ctypes.POINTER(ctypes.c_size_t)]
+        L.loopvq_lloyd_workspace.restype = _I32
+        L.loopvq_lloyd_step.argtypes = [cfgp, ctypes.POINTER(loopvq_lloyd_args), _P]
+        L.loopvq_lloyd_step.restype = _I32
+        L.loopvq_lloyd_update.argtypes = [cfgp, ctypes.POINTER(loopvq_lloyd_args), _P]
+        L.loopvq_lloyd_update.restype = _I32
         L.loopvq_decode_attn_workspace.argtypes = [cfgp, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]
         L.loopvq_decode_attn_workspace.restype = _I32
         L.loopvq_decode_attn.argtypes = [cfgp, ctypes.POINTER(loopvq_decode_args), _P, ctypes.c_size_t, _P]
@@ -197,6 +212,39 @@ def loopvq_evict(cfg, *, batch, max_pages_per_seq, num_pages, k_ring, v_ring, ri
                           norms_v=_ptr(norms_v), pool=_ptr(pool), out_idx=_ptr(out_idx),
                           rerank_count=_ptr(rerank_count))
     _check(lib().loopvq_evict(ctypes.byref(cfg), ctypes.byref(a), _stream(stream)))
+
+
+def loopvq_lloyd_workspace(cfg, n_samples: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().loopvq_lloyd_workspace(ctypes.byref(cfg), n_samples, ctypes.byref(n)))
+    return n.value
+
+
+def _lloyd_args(layer, cb_set, n_samples, src, stride_loop, stride_token, stride_head, weight, cb, cb_norms, assign,
+                workspace, workspace_bytes, cluster_weight, distortion, rerank_count):
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return loopvq_lloyd_args(layer=layer, cb_set=cb_set, n_samples=n_samples, src=_ptr(src), stride_loop=stride_loop,
+                             stride_token=stride_token, stride_head=stride_head, weight=_ptr(weight), cb=_ptr(cb),
+                             cb_norms=_ptr(cb_norms), assign=_ptr(assign), cluster_weight=_ptr(cluster_weight),
+                             distortion=_ptr(distortion), workspace=_ptr(workspace), workspace_bytes=workspace_bytes,
+                             rerank_count=_ptr(rerank_count))
+
+
+def loopvq_lloyd_step(cfg, *, layer, cb_set, n_samples, src, stride_loop, stride_token, stride_head, weight, cb,
+                      cb_norms, assign, workspace, workspace_bytes=None, cluster_weight=None, distortion=None,
+                      rerank_count=None, stream=None) -> None:
+    a = _lloyd_args(layer, cb_set, n_samples, src, stride_loop, stride_token, stride_head, weight, cb, cb_norms,
+                    assign, workspace, workspace_bytes, cluster_weight, distortion, rerank_count)
+    _check(lib().loopvq_lloyd_step(ctypes.byref(cfg), ctypes.byref(a), _stream(stream)))
+
+
+def loopvq_lloyd_update(cfg, *, layer, cb_set, n_samples, src, stride_loop, stride_token, stride_head, weight, cb,
+                        cb_norms, assign, workspace, workspace_bytes=None, cluster_weight=None, distortion=None,
+                        stream=None) -> None:
+    a = _lloyd_args(layer, cb_set, n_samples, src, stride_loop, stride_token, stride_head, weight, cb, cb_norms,
+                    assign, workspace, workspace_bytes, cluster_weight, distortion, None)
+    _check(lib().loopvq_lloyd_update(ctypes.byref(cfg), ctypes.byref(a), _stream(stream)))
 
 
 def loopvq_decode_attn_workspace(cfg, batch: int, max_seq_len: int) -> int:

@@ -139,6 +139,51 @@ lvq::EncodeParams encode_params(const loopvq_config* cfg, const Sizes& z, int32_
   return p;
 }
 
+// Row partition of the Lloyd sums kernel: one 1024-thread workgroup per CU (its fp64
+// accumulator fills most of the LDS), so aim at 256 workgroups, with at least 2048 rows each.
+struct LloydPlan {
+  int chunks_a, rows_a;
+  size_t sums_doubles, dist_doubles, w_doubles;
+  size_t bytes() const { return (sums_doubles + dist_doubles + w_doubles) * sizeof(double); }
+};
+
+LloydPlan lloyd_plan(const loopvq_config* cfg, const Sizes& z, int32_t n) {
+  LloydPlan pl;
+  const int per_chunk = cfg->num_kv_heads * cfg->loop_group * (cfg->head_dim / 64);
+  const int64_t by_rows = std::max<int64_t>(1, (int64_t(n) + 2047) / 2048);
+  pl.chunks_a = (int)std::max<int64_t>(1, std::min<int64_t>((256 + per_chunk - 1) / per_chunk, by_rows));
+  pl.rows_a = (int)((int64_t(n) + pl.chunks_a - 1) / pl.chunks_a);
+  const size_t hk = size_t(pl.chunks_a) * cfg->num_kv_heads;
+  pl.sums_doubles = hk * cfg->loop_group * cfg->head_dim * z.K;
+  pl.dist_doubles = hk * cfg->loop_group * z.ng;
+  pl.w_doubles = hk * z.ng * z.K;
+  return pl;
+}
+
+loopvq_status check_lloyd(const loopvq_config* cfg, const loopvq_lloyd_args* a) {
+  loopvq_status s = check_config(cfg);
+  if (s) return s;
+  if (!a) return fail(LOOPVQ_ERR_INVALID_ARG, "args is NULL");
+  if ((s = check_supported(cfg))) return s;
+  const Sizes z = sizes_of(cfg);
+  if (a->layer < 0 || a->layer >= cfg->num_layers) return fail(LOOPVQ_ERR_INVALID_ARG, "layer out of range");
+  if (a->cb_set < 0 || a->cb_set >= z.Jcb)
+    return fail(LOOPVQ_ERR_INVALID_ARG, "cb_set %d out of range [0, %d)", a->cb_set, z.Jcb);
+  if (a->n_samples < 0) return fail(LOOPVQ_ERR_INVALID_ARG, "n_samples must be >= 0");
+  if (!a->src || !a->weight || !a->cb || !a->cb_norms || !a->assign || !a->workspace)
+    return fail(LOOPVQ_ERR_INVALID_ARG, "src, weight, cb, cb_norms, assign and workspace must not be NULL");
+  if (!aligned(a->src, 16) || a->stride_loop % 8 || a->stride_token % 8 || a->stride_head % 8)
+    return fail(LOOPVQ_ERR_MISALIGNED, "src must be 16-byte aligned and its strides multiples of 8 elements");
+  if (!aligned(a->weight, 16) || !aligned(a->assign, 16) || !aligned(a->cb, 16) || !aligned(a->cb_norms, 16) ||
+      !aligned(a->workspace, 16) || (a->cluster_weight && !aligned(a->cluster_weight, 8)) ||
+      (a->distortion && !aligned(a->distortion, 8)) || (a->rerank_count && !aligned(a->rerank_count, 8)))
+    return fail(LOOPVQ_ERR_MISALIGNED, "weight, assign, cb, cb_norms and workspace must be 16-byte aligned, the "
+                                       "optional outputs 8-byte aligned");
+  const size_t need = lloyd_plan(cfg, z, a->n_samples).bytes();
+  if (a->workspace_bytes < need) return fail(LOOPVQ_ERR_WORKSPACE, "workspace too small: %zu bytes needed", need);
+  return LOOPVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -206,10 +251,12 @@ loopvq_status loopvq_encode(const loopvq_config* cfg, const loopvq_encode_args* 
   if (a->loop_group < 0 || a->loop_group >= z.J) return fail(LOOPVQ_ERR_INVALID_ARG, "loop_group out of range");
   if (a->kind != 0 && a->kind != 1) return fail(LOOPVQ_ERR_INVALID_ARG, "kind must be 0 (K) or 1 (V)");
   if (a->n_tokens < 0) return fail(LOOPVQ_ERR_INVALID_ARG, "n_tokens must be >= 0");
-  if (a->batch < 1 || a->max_pages_per_seq < 1 || a->num_pages < 1)
+  if (a->pool && (a->batch < 1 || a->max_pages_per_seq < 1 || a->num_pages < 1))
     return fail(LOOPVQ_ERR_INVALID_ARG, "batch, max_pages_per_seq and num_pages must be >= 1");
-  if (!a->src || !a->seq_id || !a->vq_pos || !a->block_table || !a->cb || !a->cb_norms || !a->pool)
-    return fail(LOOPVQ_ERR_INVALID_ARG, "src, seq_id, vq_pos, block_table, cb, cb_norms and pool must not be NULL");
+  if (!a->src || !a->cb || !a->cb_norms) return fail(LOOPVQ_ERR_INVALID_ARG, "src, cb and cb_norms must not be NULL");
+  if (a->pool && (!a->seq_id || !a->vq_pos || !a->block_table))
+    return fail(LOOPVQ_ERR_INVALID_ARG, "seq_id, vq_pos and block_table must not be NULL when pool is given");
+  if (!a->pool && !a->out_idx) return fail(LOOPVQ_ERR_INVALID_ARG, "an encode without a pool needs out_idx");
   const int vec = cfg->chans_per_group;  // elements per aligned load (8 B at c=4, 16 B at c=8)
   if (!aligned(a->src, 2 * vec) || a->stride_loop % vec || a->stride_token % vec || a->stride_head % vec)
     return fail(LOOPVQ_ERR_MISALIGNED, "src must be %d-byte aligned and its strides multiples of %d elements",
@@ -219,7 +266,8 @@ loopvq_status loopvq_encode(const loopvq_config* cfg, const loopvq_encode_args* 
   if (a->out_idx && !aligned(a->out_idx, 4)) return fail(LOOPVQ_ERR_MISALIGNED, "out_idx must be 4-byte aligned");
   if (a->rerank_count && !aligned(a->rerank_count, 8))
     return fail(LOOPVQ_ERR_MISALIGNED, "rerank_count must be 8-byte aligned");
-  lvq::EncodeParams p = encode_params(cfg, z, a->batch, a->max_pages_per_seq, a->num_pages);
+  lvq::EncodeParams p = a->pool ? encode_params(cfg, z, a->batch, a->max_pages_per_seq, a->num_pages)
+                                : encode_params(cfg, z, 1, 1, 1);
   p.n_slices = 1;
   p.layer = a->layer;
   p.loop_group = a->loop_group;
@@ -242,6 +290,76 @@ loopvq_status loopvq_encode(const loopvq_config* cfg, const loopvq_encode_args* 
   const hipError_t e = lvq::launch_encode(p, cfg->chans_per_group, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LOOPVQ_ERR_HIP, "encode launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+loopvq_status loopvq_lloyd_workspace(const loopvq_config* cfg, int32_t n_samples, size_t* bytes) {
+  loopvq_status s = check_config(cfg);
+  if (s) return s;
+  if ((s = check_supported(cfg))) return s;
+  if (!bytes) return fail(LOOPVQ_ERR_INVALID_ARG, "bytes is NULL");
+  if (n_samples < 0) return fail(LOOPVQ_ERR_INVALID_ARG, "n_samples must be >= 0");
+  *bytes = lloyd_plan(cfg, sizes_of(cfg), n_samples).bytes();
+  return ok();
+}
+
+loopvq_status loopvq_lloyd_update(const loopvq_config* cfg, const loopvq_lloyd_args* a, void* stream) {
+  loopvq_status s = check_lloyd(cfg, a);
+  if (s) return s;
+  const Sizes z = sizes_of(cfg);
+  const LloydPlan pl = lloyd_plan(cfg, z, a->n_samples);
+  const int64_t set = int64_t(a->layer) * z.Jcb + a->cb_set;
+  const int64_t set_codes = int64_t(cfg->num_kv_heads) * z.ng * z.K;
+  lvq::LloydParams p{};
+  p.n = a->n_samples;
+  p.Hkv = cfg->num_kv_heads;
+  p.NG = z.ng;
+  p.G = cfg->loop_group;
+  p.d = cfg->head_dim;
+  p.E = z.E;
+  p.chunks_a = pl.chunks_a;
+  p.rows_a = pl.rows_a;
+  p.src = a->src;
+  p.stride_loop = a->stride_loop;
+  p.stride_token = a->stride_token;
+  p.stride_head = a->stride_head;
+  p.weight = a->weight;
+  p.assign = a->assign;
+  p.cb = a->cb + set * set_codes * z.E;
+  p.norms = a->cb_norms + set * set_codes;
+  p.part_sums = (double*)a->workspace;
+  p.part_dist = p.part_sums + pl.sums_doubles;
+  p.part_w = p.part_dist + pl.dist_doubles;
+  p.cluster_weight = a->cluster_weight;
+  p.distortion = a->distortion;
+  const hipError_t he = lvq::launch_lloyd(p, cfg->chans_per_group, (hipStream_t)stream);
+  if (he != hipSuccess) return fail(LOOPVQ_ERR_HIP, "lloyd update launch: %s", hipGetErrorString(he));
+  return ok();
+}
+
+loopvq_status loopvq_lloyd_step(const loopvq_config* cfg, const loopvq_lloyd_args* a, void* stream) {
+  loopvq_status s = check_lloyd(cfg, a);
+  if (s) return s;
+  if (a->n_samples > 0) {   // the assignment: the encode kernels, without a pool
+    const Sizes z = sizes_of(cfg);
+    lvq::EncodeParams e = encode_params(cfg, z, 1, 1, 1);
+    e.n_slices = 1;
+    e.layer = a->layer;
+    e.loop_group = a->cb_set;   // selects the codebook set; with no pool nothing else reads it
+    e.kind = 0;
+    e.n_tokens = a->n_samples;
+    e.src = e.src_v = a->src;
+    e.stride_loop = a->stride_loop;
+    e.stride_token = a->stride_token;
+    e.stride_head = a->stride_head;
+    e.cb = e.cb_v = a->cb;
+    e.norms = e.norms_v = a->cb_norms;
+    e.pool = nullptr;
+    e.out_idx = a->assign;
+    e.rerank_count = a->rerank_count;
+    const hipError_t he = lvq::launch_encode(e, cfg->chans_per_group, (hipStream_t)stream);
+    if (he != hipSuccess) return fail(LOOPVQ_ERR_HIP, "lloyd assignment launch: %s", hipGetErrorString(he));
+  }
+  return loopvq_lloyd_update(cfg, a, stream);
 }
 
 loopvq_status loopvq_evict(const loopvq_config* cfg, const loopvq_evict_args* a, void* stream) {

@@ -59,15 +59,6 @@ __device__ __forceinline__ float key_value(float k) { return __uint_as_float(__f
 // last word of a raw (unstructured, byte-addressed) buffer resource on CDNA
 constexpr int kRawBufferWord3 = 0x00020000;
 
-// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.  Block L runs
-// on XCD L % 8; give XCD x the contiguous range of logical blocks that starts where the
-// ranges of XCDs 0..x-1 end, so that an XCD works on few kv-heads and its L2 holds their
-// codebooks.  The map is a bijection of [0, n).
-__device__ __forceinline__ int xcd_local_block(int L, int n) {
-  const int x = L & 7, per = n >> 3, rem = n & 7;
-  return x * per + (x < rem ? x : rem) + (L >> 3);
-}
-
 // channel groups per kv-head the kernels take (d / c <= 32)
 constexpr int kMaxGroups = 32;
 
@@ -136,6 +127,7 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
   // clamped addresses, then validated.)
   auto slot_ok = [&](int r) { return !p.row_slot || (p.row_slot[r] >= 0 && p.row_slot[r] < p.R); };
   auto slot_of = [&](int r) -> int64_t {   // the same for one row, with plain loads (re-rank)
+    if (!p.pool) return -1;
     const int sq = p.seq_id ? p.seq_id[r] : r, u = p.vq_pos[r];
     if (!slot_ok(r) || sq < 0 || sq >= p.batch || u < 0 || (u >> p.pt_shift) >= p.max_pages) return -1;
     const int page = p.block_table[(int64_t)sq * p.max_pages + (u >> p.pt_shift)];
@@ -144,7 +136,10 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
     return (int64_t)page * p.page_bytes + (int64_t)kind * p.kind_bytes + (w >> 2) * (NG >> 2) * 16 + (w & 3) * 4;
   };
   int64_t slot[TT];
-  {
+  if (!p.pool) {   // assignment only (no pool, no positions): the indices go to out_idx alone
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) slot[tt] = -1;
+  } else {
     int seq[TT], u[TT], page[TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {

@@ -99,11 +99,28 @@ struct PrepareParams {
   float* norms;
 };
 
+struct LloydParams {
+  int n, Hkv, NG, G, d, E;   // samples, kv-heads, groups, loop steps, head_dim, c * G
+  int chunks_a, rows_a;      // lloyd_sums: rows [chunk * rows_a, ...) per chunk
+  const uint16_t* src;       // sample planes: plane tau of row r, kv-head h at
+  int64_t stride_loop, stride_token, stride_head;   //  src + tau*stride_loop + r*stride_token + h*stride_head
+  const float* weight;       // [n][Hkv][NG]
+  const int32_t* assign;     // [n][Hkv][NG]
+  uint16_t* cb;              // the set's canonical codebooks [Hkv][NG][K][E] (updated)
+  float* norms;              // the set's squared norms [Hkv][NG][K] (recomputed)
+  double* part_sums;         // [chunks_a][Hkv][G][d/64][64/c][c][K]
+  double* part_dist;         // [chunks_a][Hkv][G][NG]
+  double* part_w;            // [chunks_a][Hkv][NG][K]
+  double* cluster_weight;    // [Hkv][NG][K] or nullptr
+  double* distortion;        // [Hkv][NG] or nullptr
+};
+
 // Launchers (defined next to their kernels).  Return hipSuccess or the launch error.
 hipError_t launch_decode(const DecodeParams& p, int ng, int c, hipStream_t stream);
 hipError_t launch_encode(const EncodeParams& p, int c, hipStream_t stream);
 hipError_t launch_extend(const ExtendParams& p, int ng, int c, hipStream_t stream);
 hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream);
+hipError_t launch_lloyd(const LloydParams& p, int c, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Device helpers
@@ -115,6 +132,26 @@ __device__ __forceinline__ float bf16_at(const uint16_t* p) { return __uint_as_f
 // DPP controls (GCN/CDNA encoding)
 constexpr int dpp_quad(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
 constexpr int kDppRowHalfMirror = 0x141;
+
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.  Block L runs
+// on XCD L % 8; give XCD x the contiguous range of logical blocks that starts where the
+// ranges of XCDs 0..x-1 end, so that an XCD works on few kv-heads (or rows) and its L2 holds what
+// they share.  The map is a bijection of [0, n).
+__device__ __forceinline__ int xcd_local_block(int L, int n) {
+  const int x = L & 7, per = n >> 3, rem = n & 7;
+  return x * per + (x < rem ? x : rem) + (L >> 3);
+}
+
+// Squared norm of one codeword of E bf16 elements, fp32, summed in element order with fused
+// multiply-adds: the encode screen's seed.  Every writer of the norms uses this one routine.
+__device__ __forceinline__ float codeword_norm(const uint16_t* row, int E) {
+  float acc = 0.f;
+  for (int e = 0; e < E; ++e) {
+    const float v = bf16_at(row + e);
+    acc = fmaf(v, v, acc);
+  }
+  return acc;
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {

@@ -29,13 +29,7 @@ __global__ void __launch_bounds__(256) prepare_norms(PrepareParams p) {
   const int64_t total = p.sets * p.NG * p.K;
   const int E = p.c * p.G;
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
-    const uint16_t* row = p.cb + idx * E;
-    float acc = 0.f;
-    for (int e = 0; e < E; ++e) {
-      const float v = bf16_at(row + e);
-      acc = fmaf(v, v, acc);
-    }
-    p.norms[idx] = acc;
+    p.norms[idx] = codeword_norm(p.cb + idx * E, E);
   }
 }
 

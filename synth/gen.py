@@ -44,7 +44,7 @@ AR_RHO = 0.9
 AR_INNOV = float(np.sqrt(1.0 - AR_RHO * AR_RHO))
 
 # stream ids
-S_DATA, S_CODEBOOK, S_QUERY, S_SCALES, S_ROT, S_INDEX = 1, 2, 3, 4, 5, 6
+S_DATA, S_CODEBOOK, S_QUERY, S_SCALES, S_ROT, S_INDEX, S_WEIGHT = 1, 2, 3, 4, 5, 6, 7
 
 _TABLE = None
 
@@ -95,6 +95,19 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return b.view(np.float32).astype(np.float64)
+
+
+def sample_weights(wl: Workload, n: int, salt: int = 0) -> np.ndarray:
+    """fp32 [n][Hkv][NG] per-sample weights standing in for Fisher information in codebook
+    learning: (1 + m) * 2**-23 with m the top 24 bits of the stream (so in (0, 2], exact in
+    fp32), and 0 for one sample in 16 (the low 4 bits zero)."""
+    cnt = n * wl.kv_heads * wl.groups
+    with np.errstate(over="ignore"):
+        key = stream_key(wl, S_WEIGHT) + np.uint64(salt) * GAMMA
+    u = uniform_u64(key, np.arange(cnt, dtype=np.uint64))
+    w = ((u >> np.uint64(40)).astype(np.float64) + 1.0) * 2.0 ** -23
+    w[(u & np.uint64(15)) == 0] = 0.0
+    return w.astype(np.float32).reshape(n, wl.kv_heads, wl.groups)
 
 
 def loops_padded(T: int) -> int:

@@ -39,6 +39,7 @@ def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(lvq.loopvq_decode_args) == 6 * 4 + 8 + 10 * 8 + 8 + 8 + 8 + 8
     assert ctypes.sizeof(lvq.loopvq_evict_args) == 4 + 4 + 8 + 12 * 8
     assert ctypes.sizeof(lvq.loopvq_extend_args) == 6 * 4 + 8 + 14 * 8 + 8 + 8
+    assert ctypes.sizeof(lvq.loopvq_lloyd_args) == 3 * 4 + 4 + 8 + 3 * 8 + 7 * 8 + 8 + 8
 
 
 @pytest.mark.parametrize("wl", W.ALL, ids=[w.name for w in W.ALL])
@@ -178,6 +179,10 @@ def _encode_kw(**over):
     (dict(src=FAKE + 4), lvq.LOOPVQ_ERR_MISALIGNED),
     (dict(stride_token=2050), lvq.LOOPVQ_ERR_MISALIGNED),
     (dict(cb=FAKE + 8), lvq.LOOPVQ_ERR_MISALIGNED),
+    (dict(seq_id=None), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(block_table=None), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(pool=None), lvq.LOOPVQ_ERR_INVALID_ARG),                 # no pool and no out_idx
+    (dict(pool=None, out_idx=FAKE + 2), lvq.LOOPVQ_ERR_MISALIGNED),   # assignment only: out_idx checked
 ])
 def test_encode_rejects_before_launch(over, status):
     cfg = lvq.make_config(W.LAYER_4K)
@@ -245,6 +250,56 @@ def test_extend_rejects_before_launch(over, status):
     with pytest.raises(lvq.LoopVQError) as e:
         lvq.loopvq_extend_attn(cfg, **_extend_kw(**over))
     assert e.value.status == status
+
+
+def _lloyd_kw(**over):
+    kw = dict(layer=0, cb_set=0, n_samples=1000, src=FAKE, stride_loop=1000 * 16 * 128, stride_token=16 * 128,
+              stride_head=128, weight=FAKE, cb=FAKE, cb_norms=FAKE, assign=FAKE, workspace=FAKE,
+              workspace_bytes=1 << 40, stream=0)
+    kw.update(over)
+    return kw
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(layer=1), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(cb_set=1), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(n_samples=-1), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(weight=None), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(assign=None), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(workspace=None), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(src=FAKE + 8), lvq.LOOPVQ_ERR_MISALIGNED),
+    (dict(stride_token=16 * 128 + 4), lvq.LOOPVQ_ERR_MISALIGNED),
+    (dict(weight=FAKE + 8), lvq.LOOPVQ_ERR_MISALIGNED),
+    (dict(distortion=FAKE + 4), lvq.LOOPVQ_ERR_MISALIGNED),
+    (dict(workspace_bytes=64), lvq.LOOPVQ_ERR_WORKSPACE),
+])
+def test_lloyd_rejects_before_launch(over, status):
+    cfg = lvq.make_config(W.LAYER_4K)
+    with pytest.raises(lvq.LoopVQError) as e:
+        lvq.loopvq_lloyd_step(cfg, **_lloyd_kw(**over))
+    assert e.value.status == status
+    with pytest.raises(lvq.LoopVQError) as e:
+        lvq.loopvq_lloyd_update(cfg, **_lloyd_kw(**over))
+    assert e.value.status == status
+
+
+def test_lloyd_workspace_sizes():
+    cfg = lvq.make_config(W.LAYER_4K)
+    wl = W.LAYER_4K
+    sizes = [lvq.loopvq_lloyd_workspace(cfg, n) for n in (0, 1, 5000, 100_000, 10_000_000)]
+    assert all(s % 16 == 0 and s > 0 for s in sizes)
+    assert sizes == sorted(sizes) and sizes[-1] == sizes[-2], "partials are capped by the workgroup count"
+    # at least one set of partial sums: every (kv-head, loop step, channel, codeword) in fp64
+    assert sizes[0] >= wl.kv_heads * wl.loop_group * wl.head_dim * wl.codewords * 8
+    with pytest.raises(lvq.LoopVQError):
+        lvq.loopvq_lloyd_workspace(cfg, -1)
+    # per-group codebooks: cb_set ranges over the loop groups [0, J)
+    pg = lvq.make_config(W.DEEP_8K)
+    pg.codebook_per_loop_group = 1
+    for bad in (W.DEEP_8K.loop_groups, -1):
+        with pytest.raises(lvq.LoopVQError) as e:
+            lvq.loopvq_lloyd_step(pg, **_lloyd_kw(cb_set=bad, stride_loop=1000 * 32 * 128, stride_token=32 * 128))
+        assert e.value.status == lvq.LOOPVQ_ERR_INVALID_ARG
 
 
 def test_codebook_prepare_rejects():

@@ -76,3 +76,14 @@ def test_random_indices_range_and_shape():
 def test_ragged_lengths():
     n = gen.context_lengths(W.LAYER_4K, ragged=True, seed=1)
     assert n[0] == 4096 and n.min() >= 1 and n.max() <= 4096 and len(n) == 32
+
+
+def test_sample_weights_range_zero_share_and_exactness():
+    w = gen.sample_weights(W.LAYER_4K, 4000)
+    assert w.shape == (4000, W.LAYER_4K.kv_heads, W.LAYER_4K.groups) and w.dtype == np.float32
+    assert (w >= 0).all() and (w <= 2).all()
+    assert abs((w == 0).mean() - 1 / 16) < 0.01
+    nz = w[w > 0].astype(np.float64)
+    assert np.array_equal(nz * 2 ** 23, np.round(nz * 2 ** 23)), "weights are multiples of 2^-23"
+    assert np.array_equal(gen.sample_weights(W.LAYER_4K, 100), w[:100]), "counter-addressed"
+    assert not np.array_equal(gen.sample_weights(W.LAYER_4K, 100, salt=1), w[:100])
