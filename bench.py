@@ -185,6 +185,84 @@ class Bench:
             self.evict()
 
 
+def parse_plan(text: str, wl):
+    """Per-(layer, loop range) choice of (c, G): layers separated by '/', each a comma list of
+    'LOOPS:cxG' segments covering the layer's loop steps in order (LOOPS % G == 0), e.g.
+    '8:4x4,24:8x4/32:8x2/32:4x8/32:8x4'.  A layer list of one entry applies to every layer.
+    Returns [[(loops, c, G)]] per layer."""
+    layers = []
+    for lt in text.split("/"):
+        segs = []
+        for st in lt.split(","):
+            n, cg = st.split(":")
+            c, G = cg.lower().split("x")
+            segs.append((int(n), int(c), int(G)))
+        layers.append(segs)
+    if len(layers) == 1:
+        layers = layers * wl.layers
+    if len(layers) != wl.layers:
+        raise ValueError(f"plan has {len(layers)} layers, the workload {wl.layers}")
+    for segs in layers:
+        if sum(n for n, _, _ in segs) != wl.loops or any(n % G for n, _, G in segs):
+            raise ValueError(f"plan segments {segs} must cover {wl.loops} loop steps in whole loop groups")
+    return layers
+
+
+def plan_bits_per_elem(plan, index_bits: int) -> float:
+    """Index bits per cached element, averaged over every (layer, loop step)."""
+    tot = sum(n for segs in plan for n, _, _ in segs)
+    return sum(n * index_bits / (c * G) for segs in plan for n, c, G in segs) / tot
+
+
+class MixedBench:
+    """A stack whose (layer, loop range) segments each pick their own (c, G): one config, pool,
+    codebook set and windows per segment; decode (l, t) runs on the segment holding loop step t,
+    eviction runs once per segment."""
+
+    def __init__(self, wl, plan):
+        self.wl, self.plan = wl, plan
+        self.segs = []      # per layer: [(start, Bench)]
+        for l, segs in enumerate(plan):
+            row, start = [], 0
+            for n, c, G in segs:
+                sub = wl.with_(name=f"{wl.name}_l{l}_t{start}_c{c}g{G}", layers=1, loops=n, chans=c, loop_group=G,
+                               wid=wl.wid * 64 + l * 8 + len(row))
+                log(f"segment layer {l} loops [{start}, {start + n}) c={c} G={G}")
+                row.append((start, Bench(sub)))
+                start += n
+            self.segs.append(row)
+        self.torch = self.segs[0][0][1].torch
+
+    def decode(self, l, t):
+        for start, b in reversed(self.segs[l]):
+            if t >= start:
+                b.decode(0, t - start)
+                return
+
+    def step(self, events=None, evict_events=None):
+        E = self.torch.cuda.Event
+        for t in range(self.wl.loops):
+            for l in range(self.wl.layers):
+                if events is not None:
+                    e0, e1 = E(enable_timing=True), E(enable_timing=True)
+                    e0.record()
+                    self.decode(l, t)
+                    e1.record()
+                    events.append((e0, e1))
+                else:
+                    self.decode(l, t)
+        if evict_events is not None:
+            e0 = E(enable_timing=True)
+            e0.record()
+        for row in self.segs:
+            for _, b in row:
+                b.evict()
+        if evict_events is not None:
+            e1 = E(enable_timing=True)
+            e1.record()
+            evict_events.append((e0, e1))
+
+
 def cpu_baseline(wl, seconds: float) -> dict:
     """The CPU oracle (fp64, single BLAS thread) on sampled decode queries of the same workload."""
     from threadpoolctl import threadpool_limits
@@ -671,6 +749,11 @@ def main():
                     help="time extend (chunked prefill) attention over a packed cache instead of the decode step "
                          "(default workload for this mode: layer16h_d128_b32_n4k)")
     ap.add_argument("--chunk", type=int, default=512, help="chunk rows per sequence for --extend")
+    ap.add_argument("--cb-per-loop-group", action="store_true",
+                    help="decode mode: one codebook set per loop group instead of one shared by all loop groups")
+    ap.add_argument("--plan", default=None,
+                    help="decode mode: per-(layer, loop range) choice of (c, G), e.g. '8:4x4,24:8x4' "
+                         "(layers separated by '/'; one entry applies to every layer)")
     ap.add_argument("--lloyd", action="store_true",
                     help="time one weighted Lloyd iteration of one codebook set instead of the decode step "
                          "(default workload for this mode: deep4x32_h32_d128_b16_n8k)")
@@ -697,8 +780,11 @@ def main():
     import torch
     from synth import workloads as W
     wl = W.BY_NAME[args.workload]
+    if args.cb_per_loop_group:
+        wl = wl.with_(name=wl.name + "_cbj", codebook_per_loop_group=True)
     torch.cuda.set_device(0)
-    bench = Bench(wl)
+    plan = parse_plan(args.plan, wl) if args.plan else None
+    bench = MixedBench(wl, plan) if plan else Bench(wl)
     for _ in range(args.warmup):
         bench.step()
     torch.cuda.synchronize()
@@ -715,12 +801,18 @@ def main():
     wall = time.perf_counter() - t0
     step_ms = ev0.elapsed_time(ev1) / args.steps
     launch_us = np.array([a.elapsed_time(b) * 1e3 for a, b in events])
-    ab = algorithmic_bytes(wl)
+    if plan:   # bytes of a launch averaged over the segments' launches
+        ab_l = [algorithmic_bytes(wl.with_(chans=c, loop_group=G)) for segs in plan for n, c, G in segs
+                for _ in range(n)]
+        ab = {k: sum(a[k] for a in ab_l) / len(ab_l) for k in ab_l[0]}
+    else:
+        ab = algorithmic_bytes(wl)
     q_per_step = wl.layers * wl.loops * wl.queries_per_launch
     value = q_per_step / (step_ms * 1e-3)
     avg_us = float(launch_us.mean())
     achieved = ab["total"] / (avg_us * 1e-6) / 1e9
-    traffic = traffic_from_profile()
+    # the committed counter summary covers the default workload's launches only
+    traffic = traffic_from_profile() if (wl.name == DEFAULT_WORKLOAD and not plan) else None
     log(f"wall {wall:.2f}s for {args.steps} steps; launch avg {avg_us:.1f} us (p10 {np.percentile(launch_us, 10):.1f}, "
         f"p90 {np.percentile(launch_us, 90):.1f}); {achieved:.0f} GB/s")
     rec = {
@@ -731,10 +823,17 @@ def main():
                    "q_heads": wl.q_heads, "kv_heads": wl.kv_heads, "head_dim": wl.head_dim, "batch": wl.batch,
                    "context": wl.context, "prefix_tokens": wl.prefix, "recent_tokens": wl.recent,
                    "chans_per_group": wl.chans, "index_bits": wl.index_bits,
-                   "bits_per_elem": wl.index_bits / (wl.chans * wl.loop_group), "page_tokens": wl.page_tokens,
+                   "bits_per_elem": (plan_bits_per_elem(plan, wl.index_bits) if plan
+                                     else wl.index_bits / (wl.chans * wl.loop_group)),
+                   "page_tokens": wl.page_tokens,
+                   "codebook_per_loop_group": bool(wl.codebook_per_loop_group),
+                   "plan": args.plan,
                    "launches_per_step": wl.layers * wl.loops,
-                   "eviction_launches_per_step": 1,
-                   "evicted_sub_vectors_per_step": wl.layers * wl.loop_groups * 2 * wl.batch * wl.kv_heads * wl.groups},
+                   "eviction_launches_per_step": sum(len(s) for s in plan) if plan else 1,
+                   "evicted_sub_vectors_per_step": (
+                       sum((n // G) * 2 * wl.batch * wl.kv_heads * (wl.head_dim // c)
+                           for segs in plan for n, c, G in segs) if plan
+                       else wl.layers * wl.loop_groups * 2 * wl.batch * wl.kv_heads * wl.groups)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
         "decode_launch_us": {"mean": avg_us, "p10": float(np.percentile(launch_us, 10)),
@@ -744,7 +843,9 @@ def main():
         "step_gbps": ab["total"] * wl.layers * wl.loops / (step_ms * 1e-3) / 1e9,
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        # with a plan: the oracle on the workload of layer 0's first segment
+        base = wl.with_(chans=plan[0][0][1], loop_group=plan[0][0][2]) if plan else wl
+        rec["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
 
 

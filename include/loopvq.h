@@ -54,8 +54,11 @@ typedef int32_t loopvq_status;
  *   power of two >= 64), codebook_per_loop_group (0: one codebook set per
  *   (layer, kv-head, group) shared by all loop groups, Jcb = 1; 1: one per loop
  *   group, Jcb = J).
- * Kernels are built for b = 8, (c, G) in {(4,4), (8,4)}, NG in {16, 32}; other
- * valid shapes return LOOPVQ_ERR_UNSUPPORTED from encode / decode. */
+ * Kernels are built for b = 8, (c, G) in {(4,4), (8,4), (8,2), (4,8)} (sub-vectors
+ * of 16 or 32 elements) and (c, d) in {(4,64), (4,128), (8,128)}; other valid
+ * shapes return LOOPVQ_ERR_UNSUPPORTED from the compute entry points.  A model
+ * that picks (c, G) per layer or per loop group uses one config (and one pool
+ * and codebook set) per distinct choice. */
 typedef struct loopvq_config {
   int32_t num_layers;
   int32_t num_loops;

@@ -66,7 +66,13 @@ loopvq_status check_config(const loopvq_config* c) {
 loopvq_status check_supported(const loopvq_config* c) {
   const int ng = c->head_dim / c->chans_per_group;
   if (c->index_bits != 8) return fail(LOOPVQ_ERR_UNSUPPORTED, "kernels are built for index_bits = 8 only");
-  if (c->loop_group != 4) return fail(LOOPVQ_ERR_UNSUPPORTED, "kernels are built for loop_group = 4 only");
+  const int E = c->chans_per_group * c->loop_group;
+  const bool okg = c->loop_group == 4 || (c->loop_group == 2 && c->chans_per_group == 8) ||
+                   (c->loop_group == 8 && c->chans_per_group == 4);
+  if (!okg)
+    return fail(LOOPVQ_ERR_UNSUPPORTED,
+                "kernels are built for (c, G) in {(4, 4), (8, 4), (8, 2), (4, 8)}; got (%d, %d), sub-vector length %d",
+                c->chans_per_group, c->loop_group, E);
   const bool okv = (c->chans_per_group == 4 && (ng == 16 || ng == 32)) || (c->chans_per_group == 8 && ng == 16);
   if (!okv)
     return fail(LOOPVQ_ERR_UNSUPPORTED, "kernels are built for (c, d) in {(4, 64), (4, 128), (8, 128)}; got (%d, %d)",

@@ -62,7 +62,7 @@ constexpr int kRawBufferWord3 = 0x00020000;
 // channel groups per kv-head the kernels take (d / c <= 32)
 constexpr int kMaxGroups = 32;
 
-// Bulk stage: channels [ch0, ch0 + 64) of the block's rows for the 4 loop steps, as
+// Bulk stage: channels [ch0, ch0 + 64) of the block's rows for the G loop steps, as
 // [loop step t][row r][64 channels] bf16 (128 B per row).  The 8-byte slot s (4 channels) of
 // row r sits at slot s ^ ((r >> 1) & 15) of its row, so the 32 rows that a half-wave reads at
 // one slot fall on 32 distinct 8-byte bank pairs.
@@ -72,9 +72,9 @@ __device__ __forceinline__ int stage_off(int r, int t, int s) {
   return (t * ROWS + r) * 128 + ((s ^ ((r >> 1) & 15)) << 3);
 }
 
-template <int C, int TT, bool STAGE>
+template <int C, int G, int TT, bool STAGE>
 __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int groups_per_wg, int gx, int gy) {
-  constexpr int E = 4 * C;        // sub-vector length (G = 4 loop steps)
+  constexpr int E = G * C;        // sub-vector length (16 or 32)
   constexpr int NMF = E / 16;     // code MFMAs per distance tile
   constexpr int ROWS = 32 * TT;   // rows of the block
 
@@ -113,7 +113,7 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
   };
   const int pt_mask = (1 << p.pt_shift) - 1;
   const uint32_t one2 = 0x3f803f80u;   // two bf16 ones
-  __shared__ __align__(16) uint8_t stage[STAGE ? 4 * ROWS * 128 : 16];
+  __shared__ __align__(16) uint8_t stage[STAGE ? G * ROWS * 128 : 16];
   // rows whose screen is not conclusive, as (row in block) * 32 + group, re-ranked exactly
   // after the screen so that no wave holds up the others in the middle of it
   __shared__ uint16_t rr_list[ROWS * kMaxGroups];
@@ -198,9 +198,9 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
 #pragma unroll
         for (int m = 0; m < NMF; ++m) {
           uint2 lo, hi;
-          if constexpr (C == 4) {             // loop steps 2*half, 2*half+1; slot gl
-            lo = *reinterpret_cast<const uint2*>(stage + stage_off<ROWS>(r, 2 * half, gl));
-            hi = *reinterpret_cast<const uint2*>(stage + stage_off<ROWS>(r, 2 * half + 1, gl));
+          if constexpr (C == 4) {             // loop steps 4m + 2*half, +1; slot gl
+            lo = *reinterpret_cast<const uint2*>(stage + stage_off<ROWS>(r, 4 * m + 2 * half, gl));
+            hi = *reinterpret_cast<const uint2*>(stage + stage_off<ROWS>(r, 4 * m + 2 * half + 1, gl));
           } else {                            // loop step 2m + half; slots 2gl, 2gl+1
             lo = *reinterpret_cast<const uint2*>(stage + stage_off<ROWS>(r, 2 * m + half, 2 * gl));
             hi = *reinterpret_cast<const uint2*>(stage + stage_off<ROWS>(r, 2 * m + half, 2 * gl + 1));
@@ -212,7 +212,7 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
 #pragma unroll
         for (int m = 0; m < NMF; ++m) {
           if constexpr (C == 4) {
-            const int t0 = 2 * half;      // elements 8*half .. +7 = loop steps 2*half, 2*half+1
+            const int t0 = 4 * m + 2 * half;   // elements 16m + 8*half .. +7 = loop steps t0, t0 + 1
             const uint2 lo = *reinterpret_cast<const uint2*>(base + t0 * p.stride_loop + gq * 4);
             const uint2 hi = *reinterpret_cast<const uint2*>(base + (t0 + 1) * p.stride_loop + gq * 4);
             xr[tt][m] = u32x4{lo.x, lo.y, hi.x, hi.y};
@@ -225,31 +225,34 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
     }
   };
   // Fill the stage with channels [ch0, ch0 + 64) with LDS-direct dword loads: wave w copies
-  // loop step w; one instruction fills 256 consecutive stage bytes (two rows, two whole
+  // loop steps w, w + 4, ...; one instruction fills 256 consecutive stage bytes (two rows, two whole
   // 128-byte source lines), each lane fetching the source dword its stage position holds.
   // Rows past the end read the last row.
   auto stage_rows = [&](int ch0) {
     const int sl = (lane >> 1) & 15;   // stage slot of this lane
-    const uint16_t* plane = src + (int64_t)wave * p.stride_loop + (int64_t)h * p.stride_head;
-    if (row0 + ROWS <= p.n_tokens && p.stride_token < (int64_t)1 << 30) {
-      // whole block: a uniform row-pair base plus a 32-bit lane offset (which includes the
-      // channel range, so that it is not kept live outside this function)
-      const uint32_t lane_off = (uint32_t)half * (uint32_t)p.stride_token * 2u + (lane & 1) * 4 + ch0 * 2;
+#pragma unroll
+    for (int t = wave; t < G; t += 4) {
+      const uint16_t* plane = src + (int64_t)t * p.stride_loop + (int64_t)h * p.stride_head;
+      if (row0 + ROWS <= p.n_tokens && p.stride_token < (int64_t)1 << 30) {
+        // whole block: a uniform row-pair base plus a 32-bit lane offset (which includes the
+        // channel range, so that it is not kept live outside this function)
+        const uint32_t lane_off = (uint32_t)half * (uint32_t)p.stride_token * 2u + (lane & 1) * 4 + ch0 * 2;
 #pragma unroll 16
-      for (int j = 0; j < ROWS / 2; ++j) {
-        const char* rows = reinterpret_cast<const char*>(plane + (int64_t)(row0 + 2 * j) * p.stride_token);
-        const uint32_t off = ((uint32_t)(sl << 3) ^ (uint32_t)((j & 15) << 3)) + lane_off;
-        __builtin_amdgcn_global_load_lds((global_void*)(rows + off), (lds_void*)(stage + (wave * ROWS + 2 * j) * 128),
-                                         4, 0, 0);
-      }
-    } else {
-      const uint16_t* src_l = plane + ch0 + (lane & 1) * 2;
+        for (int j = 0; j < ROWS / 2; ++j) {
+          const char* rows = reinterpret_cast<const char*>(plane + (int64_t)(row0 + 2 * j) * p.stride_token);
+          const uint32_t off = ((uint32_t)(sl << 3) ^ (uint32_t)((j & 15) << 3)) + lane_off;
+          __builtin_amdgcn_global_load_lds((global_void*)(rows + off), (lds_void*)(stage + (t * ROWS + 2 * j) * 128),
+                                           4, 0, 0);
+        }
+      } else {
+        const uint16_t* src_l = plane + ch0 + (lane & 1) * 2;
 #pragma unroll 4
-      for (int j = 0; j < ROWS / 2; ++j) {
-        const int row = min(row0 + 2 * j + half, p.n_tokens - 1);
-        const uint16_t* src = src_l + (int64_t)row * p.stride_token + ((sl ^ (j & 15)) << 2);
-        __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)(stage + (wave * ROWS + 2 * j) * 128), 4, 0,
-                                         0);
+        for (int j = 0; j < ROWS / 2; ++j) {
+          const int row = min(row0 + 2 * j + half, p.n_tokens - 1);
+          const uint16_t* src = src_l + (int64_t)row * p.stride_token + ((sl ^ (j & 15)) << 2);
+          __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)(stage + (t * ROWS + 2 * j) * 128), 4, 0,
+                                           0);
+        }
       }
     }
   };
@@ -451,7 +454,7 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
     // the row's elements tau*c + i = src[tau][r][h][gq*c + i], two per word (uniform loads)
     uint32_t xw[E / 2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < G; ++t) {
       const uint32_t* xs = reinterpret_cast<const uint32_t*>(src + row_off(r) + (int64_t)t * p.stride_loop + gq * C);
 #pragma unroll
       for (int i = 0; i < C / 2; ++i) xw[t * (C / 2) + i] = xs[i];
@@ -510,8 +513,10 @@ hipError_t launch_encode(const EncodeParams& p, int c, hipStream_t stream) {
   // whole by one workgroup
   // (an eviction's rows sit at ring slots, not at a fixed row stride: always the direct path)
   const bool small = p.n_slices > 1 || (int64_t)p.n_tokens * p.Hkv < 16384;
+  // bulk rows per workgroup: the stage holds G loop steps of 64 channels per row
+  const int bulk_rows = p.G == 8 ? 64 : 128;
   const int groups_per_wg = small ? 4 : p.NG;
-  const int rows_per_wg = small ? 64 : 128;
+  const int rows_per_wg = small ? 64 : bulk_rows;
   const int gx = (p.NG + groups_per_wg - 1) / groups_per_wg;
   const int gy = (p.n_tokens + rows_per_wg - 1) / rows_per_wg;
   const int64_t blocks = (int64_t)gx * gy * p.Hkv * p.n_slices;
@@ -520,16 +525,20 @@ hipError_t launch_encode(const EncodeParams& p, int c, hipStream_t stream) {
   // the staged bulk path takes 64 channels at a time
   if (!small && (p.NG * c) % kStageCh != 0) return hipErrorInvalidValue;
   if (p.NG > kMaxGroups) return hipErrorInvalidValue;
-  if (c == 4 && small)
-    hipLaunchKernelGGL((encode_kernel<4, 2, false>), grid, dim3(256), 0, stream, p, groups_per_wg, gx, gy);
-  else if (c == 4)
-    hipLaunchKernelGGL((encode_kernel<4, 4, true>), grid, dim3(256), 0, stream, p, groups_per_wg, gx, gy);
-  else if (c == 8 && small)
-    hipLaunchKernelGGL((encode_kernel<8, 2, false>), grid, dim3(256), 0, stream, p, groups_per_wg, gx, gy);
-  else if (c == 8)
-    hipLaunchKernelGGL((encode_kernel<8, 4, true>), grid, dim3(256), 0, stream, p, groups_per_wg, gx, gy);
-  else
+#define LVQ_ENCODE(C_, G_, TT_, ST_) \
+  hipLaunchKernelGGL((encode_kernel<C_, G_, TT_, ST_>), grid, dim3(256), 0, stream, p, groups_per_wg, gx, gy)
+  if (c == 4 && p.G == 4) {
+    if (small) LVQ_ENCODE(4, 4, 2, false); else LVQ_ENCODE(4, 4, 4, true);
+  } else if (c == 8 && p.G == 4) {
+    if (small) LVQ_ENCODE(8, 4, 2, false); else LVQ_ENCODE(8, 4, 4, true);
+  } else if (c == 8 && p.G == 2) {
+    if (small) LVQ_ENCODE(8, 2, 2, false); else LVQ_ENCODE(8, 2, 4, true);
+  } else if (c == 4 && p.G == 8) {
+    if (small) LVQ_ENCODE(4, 8, 2, false); else LVQ_ENCODE(4, 8, 2, true);
+  } else {
     return hipErrorInvalidValue;
+  }
+#undef LVQ_ENCODE
   return hipGetLastError();
 }
 

@@ -46,7 +46,7 @@ __global__ void __launch_bounds__(1024, 1) lloyd_sums(LloydParams p) {
   constexpr int GPS = kSliceCh / C;          // groups in a slice
   constexpr int GPL = 8 / C;                 // groups per lane (8 channels per lane)
   constexpr int ACC = GPS * C * kCodesL;     // 16384 doubles
-  constexpr int WG_MAX = GPS / 4;            // weight groups per workgroup (G >= 4)
+  constexpr int WG_MAX = GPS / 2;            // weight groups per workgroup (G >= 2)
   constexpr int U = 4;                       // rows per lane in flight
   __shared__ __align__(16) double acc[ACC];
   __shared__ double wacc[WG_MAX * kCodesL];

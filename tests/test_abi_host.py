@@ -152,7 +152,8 @@ def test_decode_auto_split_workspace_is_checked():
 
 
 def test_unsupported_variants_rejected():
-    for over in [dict(index_bits=9), dict(loop_group=2, num_loops=4), dict(chans_per_group=8, head_dim=256)]:
+    for over in [dict(index_bits=9), dict(loop_group=2, num_loops=4), dict(chans_per_group=8, head_dim=256),
+                 dict(loop_group=8, num_loops=8, chans_per_group=8)]:
         cfg = lvq.make_config(W.LAYER_4K)
         for k, v in over.items():
             setattr(cfg, k, v)

@@ -14,15 +14,16 @@ from synth import gen  # noqa: E402
 from synth.workloads import Workload  # noqa: E402
 
 
-def _wl(c, d, per_group):
-    return Workload(name=f"evict_c{c}_d{d}_cb{int(per_group)}", layers=2, loops=8, loop_group=4, q_heads=4,
+def _wl(c, d, per_group, G=4):
+    return Workload(name=f"evict_c{c}_g{G}_d{d}_cb{int(per_group)}", layers=2, loops=8, loop_group=G, q_heads=4,
                     kv_heads=2, head_dim=d, chans=c, index_bits=8, batch=5, context=600, prefix=2, recent=8,
                     outlier_channels=4, codebook_per_loop_group=per_group, wid=7)
 
 
-@pytest.mark.parametrize("c,d,per_group", [(4, 64, False), (4, 128, True), (8, 128, False)])
-def test_evict_matches_oracle(c, d, per_group):
-    wl = _wl(c, d, per_group)
+@pytest.mark.parametrize("c,d,per_group,G", [(4, 64, False, 4), (4, 128, True, 4), (8, 128, False, 4),
+                                              (8, 128, True, 2), (4, 64, False, 8)])
+def test_evict_matches_oracle(c, d, per_group, G):
+    wl = _wl(c, d, per_group, G)
     L, T, G, J, B, Hkv, R, NG = wl.layers, wl.loops, wl.loop_group, wl.loop_groups, wl.batch, wl.kv_heads, \
         wl.recent, wl.groups
     Jcb = J if per_group else 1

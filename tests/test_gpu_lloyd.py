@@ -37,8 +37,8 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def _wl(c, d, Hkv, L=1, T=4, per_group=False):
-    return Workload(name=f"lloyd_c{c}_d{d}_h{Hkv}", layers=L, loops=T, loop_group=4, q_heads=Hkv, kv_heads=Hkv,
+def _wl(c, d, Hkv, L=1, T=4, per_group=False, G=4):
+    return Workload(name=f"lloyd_c{c}_g{G}_d{d}_h{Hkv}", layers=L, loops=T, loop_group=G, q_heads=Hkv, kv_heads=Hkv,
                     head_dim=d, chans=c, index_bits=8, batch=1, context=8192, outlier_channels=2,
                     codebook_per_loop_group=per_group, wid=11)
 
@@ -81,12 +81,21 @@ CASES = {
     # c=8, d=128, per-loop-group codebooks: set (layer 1, loop group 1) of 2 x 2
     "c8_d128_sets": (8, 128, 2, 3001, 16, 2, 8, True, 1, 1),
 }
+# other loop-group sizes (G in the last field), staged bulk assignment path
+CASES_G = {
+    "c8_g2_bulk": (8, 128, 4, 4111, 0, 1, 4, True, 0, 1, 2),
+    "c4_g8_bulk": (4, 128, 4, 4100, 8, 1, 8, False, 0, 0, 8),
+}
 
 
-@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("name", list(CASES) + list(CASES_G))
 def test_lloyd_matches_oracle(name):
-    c, d, Hkv, n, pad, L, T, per_group, layer, cb_set = CASES[name]
-    wl = _wl(c, d, Hkv, L, T, per_group)
+    if name in CASES:
+        c, d, Hkv, n, pad, L, T, per_group, layer, cb_set = CASES[name]
+        G = 4
+    else:
+        c, d, Hkv, n, pad, L, T, per_group, layer, cb_set, G = CASES_G[name]
+    wl = _wl(c, d, Hkv, L, T, per_group, G)
     NG, G, K = wl.groups, wl.loop_group, wl.codewords
     cfg = lvq.make_config(wl)
     sc = gen.scales(wl)

@@ -101,6 +101,14 @@ def test_per_loop_group_codebooks_chain():
     _chain(H.Case(wl, 0, 5, [500, 250], seed=4), decode_splits=(0,))
 
 
+@pytest.mark.parametrize("c,G,loop", [(8, 2, 3), (4, 8, 13)])
+def test_other_loop_group_sizes_chain(c, G, loop):
+    """0.5 bit as 8 channels x 2 loop steps, and 0.25 bit as 4 channels x 8 loop steps."""
+    wl = SMALL.with_(loops=16, loop_group=G, chans=c, batch=3, q_heads=4, kv_heads=2, context=600)
+    _say(f"chain c={c} G={G} loop={loop}")
+    _chain(H.Case(wl, 0, loop, [600, 73, 333], seed=9), decode_splits=(0, 3))
+
+
 def test_d64_page128_chain():
     wl = W.TINY.with_(batch=3, q_heads=2, kv_heads=2, context=800, page_tokens=128)
     _say("d64 page128 chain")
@@ -146,10 +154,12 @@ FULL = [
     (W.STACK_32K, 17, 2),
     (W.QUARTER_16K, 9, 1),
     (W.DEEP_8K, 2, 29),
+    (W.DEEP_8K.with_(codebook_per_loop_group=True), 3, 21),
 ]
 
 
-@pytest.mark.parametrize("wl,layer,loop", FULL, ids=[w.name for w, _, _ in FULL])
+@pytest.mark.parametrize("wl,layer,loop", FULL, ids=[w.name + ("_cbj" if w.codebook_per_loop_group else "")
+                                                     for w, _, _ in FULL])
 def test_full_size_decode_sampled(wl, layer, loop):
     rng = np.random.default_rng(wl.wid)
     samples = [(int(rng.integers(wl.batch)), int(rng.integers(wl.q_heads))) for _ in range(6)]
