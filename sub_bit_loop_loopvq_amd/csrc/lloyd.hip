@@ -19,8 +19,8 @@
 //
 // A workgroup of lloyd_sums reads 128 contiguous bytes (64 channels of one loop-step plane)
 // of each of its rows, so every HBM line it touches is used whole.  Its LDS accumulator is
-// [group][channel][codeword] fp64 (128 KB): the 64 lanes of one atomic add hit the bank pair
-// of their codeword index mod 32, so random codewords spread over 32 bank pairs.
+// [codeword][channel] fp64 (128 KB), and the lanes of each atomic add are given channels
+// that fall on distinct banks whatever the codewords.
 #include "lvq_common.h"
 
 namespace lvq {
@@ -66,6 +66,14 @@ __global__ void __launch_bounds__(1024, 1) lloyd_sums(LloydParams p) {
   __syncthreads();
 
   const int sub = threadIdx.x & 7;           // 8-channel piece of the slice
+  const int rs = (threadIdx.x >> 3) & 7;     // row of the lane within its wave's 8 rows
+  // Step j of the lane's 8 atomic adds takes its channel e = (j + rot) mod 8.  A 64-bit LDS
+  // access is served 16 lanes (32 banks) at a time: lanes 16m..16m+15 are rows {2m, 2m+1} x the
+  // 8 pieces, and rot = 4*sub[2] + 2*(sub[1] ^ rs[1]) + rs[0] gives those 16 lanes 16 distinct
+  // (channel mod 16), hence distinct banks, whatever the codewords (and 32 distinct channels mod
+  // 32 over lanes 32m..32m+31).
+  const int rot = (((sub >> 2) & 1) << 2) | ((((sub >> 1) ^ (rs >> 1)) & 1) << 1) | (rs & 1);
+  const uint32_t m1 = (rot & 2) ? ~0u : 0u, m2 = (rot & 4) ? ~0u : 0u, sh = (rot & 1) * 16u;
   const int gl0 = sub * GPL;                 // first group of this lane within the slice
   const int g0 = slice * GPS + gl0;
   const int64_t r_begin = (int64_t)chunk * p.rows_a;
@@ -106,19 +114,44 @@ __global__ void __launch_bounds__(1024, 1) lloyd_sums(LloydParams p) {
 #pragma unroll
       for (int gl = 0; gl < GPL; ++gl)
         if (wown[gl]) atomicAdd(&wacc[((gl0 + gl) / p.G) * kCodesL + kk[u][gl]], (double)ww[u][gl]);
-      double x2[GPL];
-#pragma unroll
-      for (int gl = 0; gl < GPL; ++gl) x2[gl] = 0.0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int gl = j / C, i = j % C;
-        const float xf = (j & 1) ? bf16_hi(xw[j >> 1]) : bf16_lo(xw[j >> 1]);
-        atomicAdd(&acc[((gl0 + gl) * C + i) * kCodesL + kk[u][gl]], (double)ww[u][gl] * (double)xf);
-        if constexpr (DIST) x2[gl] += (double)(xf * xf);   // a bf16 square is exact in fp32
-      }
       if constexpr (DIST) {
 #pragma unroll
-        for (int gl = 0; gl < GPL; ++gl) dpart[gl] += (double)ww[u][gl] * x2[gl];
+        for (int gl = 0; gl < GPL; ++gl) {
+          double x2 = 0.0;
+#pragma unroll
+          for (int i = 0; i < C; ++i) {
+            const int j = gl * C + i;
+            const float xf = (j & 1) ? bf16_hi(xw[j >> 1]) : bf16_lo(xw[j >> 1]);
+            x2 += (double)(xf * xf);   // a bf16 square is exact in fp32
+          }
+          dpart[gl] += (double)ww[u][gl] * x2;
+        }
+      }
+      // The lane's 8 channels are rotated by rot once (element j of the rotated words is channel
+      // (j + rot) mod 8), so the adds index registers statically: words rotated by rot >> 1 (bit 1:
+      // one word, bit 2: two words), then by half a word when rot is odd.  The selections are bit
+      // blends (a select between array elements would become a dynamically indexed array).
+      uint32_t t[4], rw[4], xr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t[i] = xw[i] ^ ((xw[i] ^ xw[(i + 1) & 3]) & m1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rw[i] = t[i] ^ ((t[i] ^ t[(i + 2) & 3]) & m2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xr[i] = __builtin_amdgcn_alignbit(rw[(i + 1) & 3], rw[i], sh);
+      int k0 = kk[u][0], kx = 0;
+      uint32_t w0 = __float_as_uint(ww[u][0]), wx = 0u;
+      if constexpr (GPL == 2) {
+        kx = k0 ^ kk[u][1];
+        wx = w0 ^ __float_as_uint(ww[u][1]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = (j + rot) & 7;
+        const float xf = (j & 1) ? bf16_hi(xr[j >> 1]) : bf16_lo(xr[j >> 1]);
+        const int hm = -((e >> 2) & 1);              // all ones for the lane's second group (c = 4)
+        const int k = k0 ^ (kx & hm);
+        const float w = __uint_as_float(w0 ^ (wx & (uint32_t)hm));
+        atomicAdd(&acc[k * kSliceCh + sub * 8 + e], (double)w * (double)xf);
       }
     }
   }
@@ -158,9 +191,9 @@ __global__ void __launch_bounds__(256) lloyd_update(LloydParams p) {
       for (int i = 0; i < C; ++i) S[i] = 0.0;
       for (int ch = 0; ch < p.chunks_a; ++ch) {
         const int64_t part = ((int64_t)(ch * p.Hkv + h) * p.G + tau) * slices + slice;
-        const double* s = p.part_sums + (part * GPS + gl) * C * kCodesL + k;
+        const double* s = p.part_sums + part * (GPS * C * kCodesL) + k * kSliceCh + gl * C;
 #pragma unroll
-        for (int i = 0; i < C; ++i) S[i] += s[i * kCodesL];
+        for (int i = 0; i < C; ++i) S[i] += s[i];
       }
 #pragma unroll
       for (int i = 0; i < C; ++i) {

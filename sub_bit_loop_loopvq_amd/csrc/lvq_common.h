@@ -108,7 +108,7 @@ struct LloydParams {
   const int32_t* assign;     // [n][Hkv][NG]
   uint16_t* cb;              // the set's canonical codebooks [Hkv][NG][K][E] (updated)
   float* norms;              // the set's squared norms [Hkv][NG][K] (recomputed)
-  double* part_sums;         // [chunks_a][Hkv][G][d/64][64/c][c][K]
+  double* part_sums;         // [chunks_a][Hkv][G][d/64][K][64 channels]
   double* part_dist;         // [chunks_a][Hkv][G][NG]
   double* part_w;            // [chunks_a][Hkv][NG][K]
   double* cluster_weight;    // [Hkv][NG][K] or nullptr
