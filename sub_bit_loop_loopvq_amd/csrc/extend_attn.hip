@@ -29,6 +29,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kKT = 64;        // keys per tile
 constexpr int kRows = 128;     // query rows per workgroup
@@ -116,7 +118,7 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendParams p) {
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;
 
   const int64_t bhk = (int64_t)b * p.Hkv + h;
   const uint8_t* pool_h = p.pool_lj ? p.pool_lj + (int64_t)h * p.head_stride : nullptr;
@@ -258,7 +260,11 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendParams p) {
   };
 
   // ---- one staged tile: scores, online softmax, value products --------------------------------
-  // chunk_j0 >= 0 marks chunk keys: key t is chunk token chunk_j0 + t (causal); count = valid keys
+  // chunk_j0 >= 0 marks chunk keys: key t is chunk token chunk_j0 + t (causal); count = valid keys.
+  // Rows past the chunk length compute on row 0's q and are never written, so they need no mask.
+  // The softmax reference m_ref (log2 units) moves only when a score exceeds it by more than
+  // 8: exponentials stay <= 2^8 and o, l are rescaled rarely.
+  const float cl2 = p.scale_log2;
   auto consume = [&](int count, int chunk_j0) {
     f32x16 s[2];
 #pragma unroll
@@ -278,50 +284,61 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendParams p) {
       }
       s[mb] = acc;
     }
-    // mask and scale (log2 units); token of register r of block mb: 32mb + 8(r/4) + 4half + r%4
+    // raw scores; token of register r of block mb: 32mb + 8(r/4) + 4half + r%4
+    if (count < kKT || chunk_j0 >= 0) {   // (uniform) a tile with keys to hide
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * mb + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool vis = t < count && (chunk_j0 < 0 || chunk_j0 + t <= qi);
+          s[mb][r] = vis ? s[mb][r] : -INFINITY;
+        }
+    }
     float tmax = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * mb + 8 * (r >> 2) + 4 * half + (r & 3);
-        const bool vis = active && t < count && (chunk_j0 < 0 || chunk_j0 + t <= qi);
-        const float v = vis ? s[mb][r] * p.scale_log2 : -INFINITY;
-        s[mb][r] = v;
-        tmax = fmaxf(tmax, v);
-      }
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[mb][r]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * cl2;
+    const bool move = tmax > m_ref + 8.f;       // m_ref = -inf: any visible key moves it
+    if (__builtin_amdgcn_ballot_w64(move)) {
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - tmax) : 1.f;   // m_ref = -inf -> 0
+      m_ref = move ? tmax : m_ref;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    // (no early exit: every lane takes part in the MFMAs; a row with nothing visible yet keeps
-    // m = -inf and adds zeros, using 0 as its reference so that no -inf - -inf appears)
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // m_run = -inf -> 0
-    m_run = m_new;
+    // (a row with nothing visible yet keeps m_ref = -inf and uses 0, so exp2(-inf) = 0)
+    const float nm = m_ref == -INFINITY ? 0.f : -m_ref;
     float psum = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(s[mb][r] - m_use);   // -inf -> 0
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[mb][r], cl2, nm));
         s[mb][r] = e;
         psum += e;
       }
-    }
-    l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    // O^T += V^T P^T over 4 k-steps of 16 keys
+    l_run += psum;
+    // O^T += V^T P^T over 4 k-steps of 16 keys; P = hi + lo with hi the truncated upper half and
+    // lo = P - hi (exact) rounded to bf16 by the hardware conversion: 2^-16 relative
 #pragma unroll
     for (int kst = 0; kst < kKT / 16; ++kst) {
       const int mb = kst >> 1, r0 = 8 * (kst & 1);
-      uint32_t hi[8], lo[8];
+      uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) split2(s[mb][r0 + j], hi[j], lo[j]);
-      const u32x4 bh = {hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
-      const u32x4 bl = {lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t ua = __float_as_uint(s[mb][r0 + 2 * j]), ub = __float_as_uint(s[mb][r0 + 2 * j + 1]);
+        hw[j] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
+        const f32x2 lo = {__uint_as_float(ua) - __uint_as_float(ua & 0xffff0000u),
+                          __uint_as_float(ub) - __uint_as_float(ub & 0xffff0000u)};
+        lw[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+      }
+      const u32x4 bh = {hw[0], hw[1], hw[2], hw[3]};
+      const u32x4 bl = {lw[0], lw[1], lw[2], lw[3]};
       u32x4 a[DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
