@@ -469,12 +469,12 @@ class ExtendBench:
         slice_bytes = H * lay.pool_head_stride_bytes
         self.pool = torch.randint(0, 256, (slice_bytes,), dtype=torch.uint8, device=dev, generator=g)
         sc = gen.scales(wl)
-        self.prep = []
+        self.grp = []   # the group-major codebook copies extend reads
         for kind in (0, 1):
             cb = torch.from_numpy(gen.codebooks(wl, kind, sc, layers=[0]).view(np.int16)).to(dev)
-            prep = torch.empty_like(cb)
-            lvq.loopvq_codebook_prepare(self.cfg, cb, prep, None)
-            self.prep.append(prep)
+            grp = torch.empty_like(cb)
+            lvq.loopvq_codebook_prepare_groups(self.cfg, cb, grp)
+            self.grp.append(grp)
         dg = DeviceGen(wl)
         self.win = []
         for kind in (0, 1):
@@ -501,7 +501,7 @@ class ExtendBench:
         self.lvq.loopvq_extend_attn(self.cfg, layer=0, loop=0, batch=wl.batch, chunk=self.M, q=self.q, k_new=self.kn,
                                     v_new=self.vn, seq_lens=self.lens, max_seq_len=wl.context, out=self.out,
                                     block_table=self.bt, pool=self.pool, max_pages_per_seq=self.pps,
-                                    num_pages=self.num_pages, cb_k_prep=self.prep[0], cb_v_prep=self.prep[1],
+                                    num_pages=self.num_pages, cb_k_grp=self.grp[0], cb_v_grp=self.grp[1],
                                     k_prefix=self.win[0], v_prefix=self.win[2], k_recent=self.win[1],
                                     v_recent=self.win[3], rot=self.rot)
 

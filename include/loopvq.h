@@ -128,6 +128,14 @@ loopvq_status loopvq_layout_query(const loopvq_config* cfg, int32_t batch, int64
 loopvq_status loopvq_codebook_prepare(const loopvq_config* cfg, const uint16_t* cb,
                                       uint16_t* cb_prep, float* cb_norms, void* stream);
 
+/* Group-major loop slices for extend attention: the same codewords as cb, as
+ *   cb_grp  device bf16 [L][Jcb][Hkv][G][NG][K][c]  (written),
+ * so that the c channels of group g, loop slice tau of every codeword are one
+ * contiguous K x c block.  Pointers 16-byte aligned.  Run once per codebook
+ * set, like loopvq_codebook_prepare. */
+loopvq_status loopvq_codebook_prepare_groups(const loopvq_config* cfg, const uint16_t* cb,
+                                             uint16_t* cb_grp, void* stream);
+
 /* Encode: nearest codeword (plain squared Euclidean distance, lowest index on
  * ties) of every sub-vector of n_tokens token rows, for every kv-head and
  * channel group of one (layer, loop group, kind), packed into the pool.
@@ -312,7 +320,8 @@ loopvq_status loopvq_decode_attn(const loopvq_config* cfg, const loopvq_decode_a
  *                are computed (others untouched); NULL = all M
  *   out          device fp32 [B][M][Hq][d]
  * The other fields mean what they mean for decode (windows of the same (l, t),
- * pool, prepared codebooks, rot, softmax_scale).  No workspace is needed.  The
+ * pool, rot, softmax_scale); the codebooks come in the group-major layout of
+ * loopvq_codebook_prepare_groups.  No workspace is needed.  The
  * kernel dequantizes 64-token tiles into LDS and runs both products on bf16 MFMAs,
  * splitting P (and a rotated q) into two bf16 parts so they keep fp32-level
  * accuracy. */
@@ -331,8 +340,8 @@ typedef struct loopvq_extend_args {
   const int32_t* chunk_lens;    /* device [B] or NULL */
   const int32_t* block_table;
   const uint8_t* pool;
-  const uint16_t* cb_k_prep;
-  const uint16_t* cb_v_prep;
+  const uint16_t* cb_k_grp;     /* device group-major key codebooks (loopvq_codebook_prepare_groups) */
+  const uint16_t* cb_v_grp;     /* device group-major value codebooks */
   const uint16_t* k_prefix;
   const uint16_t* v_prefix;
   const uint16_t* k_recent;

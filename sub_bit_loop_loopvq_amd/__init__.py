@@ -72,12 +72,13 @@ class loopvq_decode_args(ctypes.Structure):
 class loopvq_extend_args(ctypes.Structure):
     _fields_ = [("layer", _I32), ("loop", _I32), ("batch", _I32), ("chunk", _I32), ("max_pages_per_seq", _I32),
                 ("max_seq_len", _I32), ("num_pages", _I64), ("q", _P), ("k_new", _P), ("v_new", _P),
-                ("seq_lens", _P), ("chunk_lens", _P), ("block_table", _P), ("pool", _P), ("cb_k_prep", _P),
-                ("cb_v_prep", _P), ("k_prefix", _P), ("v_prefix", _P), ("k_recent", _P), ("v_recent", _P),
+                ("seq_lens", _P), ("chunk_lens", _P), ("block_table", _P), ("pool", _P), ("cb_k_grp", _P),
+                ("cb_v_grp", _P), ("k_prefix", _P), ("v_prefix", _P), ("k_recent", _P), ("v_recent", _P),
                 ("rot", _P), ("softmax_scale", _F32), ("out", _P)]
 
 
 EXPORTS = ("loopvq_config_check", "loopvq_bits_per_elem", "loopvq_layout_query", "loopvq_codebook_prepare",
+           "loopvq_codebook_prepare_groups",
            "loopvq_encode", "loopvq_evict", "loopvq_lloyd_workspace", "loopvq_lloyd_step",
            "loopvq_lloyd_update",
            "loopvq_decode_attn_workspace", "loopvq_decode_attn",
@@ -100,6 +101,8 @@ def lib() -> ctypes.CDLL:
         L.loopvq_layout_query.argtypes = [cfgp, _I32, _I64, ctypes.POINTER(loopvq_layout)]
         L.loopvq_layout_query.restype = _I32
         L.loopvq_codebook_prepare.argtypes, L.loopvq_codebook_prepare.restype = [cfgp, _P, _P, _P, _P], _I32
+        L.loopvq_codebook_prepare_groups.argtypes = [cfgp, _P, _P, _P]
+        L.loopvq_codebook_prepare_groups.restype = _I32
         L.loopvq_encode.argtypes = [cfgp, ctypes.POINTER(loopvq_encode_args), _P]
         L.loopvq_encode.restype = _I32
         L.loopvq_evict.argtypes = [cfgp, ctypes.POINTER(loopvq_evict_args), _P]
@@ -192,6 +195,10 @@ def loopvq_codebook_prepare(cfg, cb, cb_prep, cb_norms=None, stream=None) -> Non
                                          _stream(stream)))
 
 
+def loopvq_codebook_prepare_groups(cfg, cb, cb_grp, stream=None) -> None:
+    _check(lib().loopvq_codebook_prepare_groups(ctypes.byref(cfg), _ptr(cb), _ptr(cb_grp), _stream(stream)))
+
+
 def loopvq_encode(cfg, *, layer, loop_group, kind, n_tokens, src, stride_loop, stride_token, stride_head,
                   seq_id, vq_pos, block_table, batch, max_pages_per_seq, num_pages, cb, cb_norms, pool,
                   out_idx=None, rerank_count=None, stream=None) -> None:
@@ -271,13 +278,13 @@ def loopvq_decode_attn(cfg, *, layer, loop, batch, q, seq_lens, max_seq_len, out
 
 def loopvq_extend_attn(cfg, *, layer, loop, batch, chunk, q, k_new, v_new, seq_lens, max_seq_len, out,
                        chunk_lens=None, block_table=None, pool=None, max_pages_per_seq=0, num_pages=0,
-                       cb_k_prep=None, cb_v_prep=None, k_prefix=None, v_prefix=None, k_recent=None, v_recent=None,
+                       cb_k_grp=None, cb_v_grp=None, k_prefix=None, v_prefix=None, k_recent=None, v_recent=None,
                        rot=None, softmax_scale=0.0, stream=None) -> None:
     a = loopvq_extend_args(layer=layer, loop=loop, batch=batch, chunk=chunk, max_pages_per_seq=max_pages_per_seq,
                            max_seq_len=max_seq_len, num_pages=num_pages, q=_ptr(q), k_new=_ptr(k_new),
                            v_new=_ptr(v_new), seq_lens=_ptr(seq_lens), chunk_lens=_ptr(chunk_lens),
-                           block_table=_ptr(block_table), pool=_ptr(pool), cb_k_prep=_ptr(cb_k_prep),
-                           cb_v_prep=_ptr(cb_v_prep), k_prefix=_ptr(k_prefix), v_prefix=_ptr(v_prefix),
+                           block_table=_ptr(block_table), pool=_ptr(pool), cb_k_grp=_ptr(cb_k_grp),
+                           cb_v_grp=_ptr(cb_v_grp), k_prefix=_ptr(k_prefix), v_prefix=_ptr(v_prefix),
                            k_recent=_ptr(k_recent), v_recent=_ptr(v_recent), rot=_ptr(rot),
                            softmax_scale=softmax_scale, out=_ptr(out))
     _check(lib().loopvq_extend_attn(ctypes.byref(cfg), ctypes.byref(a), _stream(stream)))

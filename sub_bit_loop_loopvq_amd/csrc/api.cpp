@@ -247,6 +247,27 @@ loopvq_status loopvq_codebook_prepare(const loopvq_config* cfg, const uint16_t* 
   return ok();
 }
 
+loopvq_status loopvq_codebook_prepare_groups(const loopvq_config* cfg, const uint16_t* cb, uint16_t* cb_grp,
+                                             void* stream) {
+  loopvq_status s = check_config(cfg);
+  if (s) return s;
+  if (!cb || !cb_grp) return fail(LOOPVQ_ERR_INVALID_ARG, "cb and cb_grp must not be NULL");
+  if (!aligned(cb, 16) || !aligned(cb_grp, 16)) return fail(LOOPVQ_ERR_MISALIGNED, "codebook pointers must be 16-byte aligned");
+  const Sizes z = sizes_of(cfg);
+  lvq::PrepareParams p{};
+  p.sets = int64_t(cfg->num_layers) * z.Jcb * cfg->num_kv_heads;
+  p.NG = z.ng;
+  p.K = z.K;
+  p.c = cfg->chans_per_group;
+  p.G = cfg->loop_group;
+  p.d = cfg->head_dim;
+  p.cb = cb;
+  p.prep = cb_grp;
+  const hipError_t e = lvq::launch_prepare_groups(p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LOOPVQ_ERR_HIP, "codebook_prepare_groups launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 loopvq_status loopvq_encode(const loopvq_config* cfg, const loopvq_encode_args* a, void* stream) {
   loopvq_status s = check_config(cfg);
   if (s) return s;
@@ -533,12 +554,12 @@ loopvq_status loopvq_extend_attn(const loopvq_config* cfg, const loopvq_extend_a
     return fail(LOOPVQ_ERR_INVALID_ARG, "q, k_new, v_new, seq_lens and out must not be NULL");
   const bool can_vq = int64_t(a->max_seq_len) > int64_t(cfg->prefix_tokens) + cfg->recent_tokens;
   if (can_vq) {
-    if (!a->block_table || !a->pool || !a->cb_k_prep || !a->cb_v_prep)
-      return fail(LOOPVQ_ERR_INVALID_ARG, "block_table, pool and prepared codebooks must not be NULL");
+    if (!a->block_table || !a->pool || !a->cb_k_grp || !a->cb_v_grp)
+      return fail(LOOPVQ_ERR_INVALID_ARG, "block_table, pool and group-major codebooks must not be NULL");
     if (a->max_pages_per_seq < 1 || a->num_pages < 1)
       return fail(LOOPVQ_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
-    if (!aligned(a->pool, 16) || !aligned(a->cb_k_prep, 16) || !aligned(a->cb_v_prep, 16))
-      return fail(LOOPVQ_ERR_MISALIGNED, "pool and prepared codebooks must be 16-byte aligned");
+    if (!aligned(a->pool, 16) || !aligned(a->cb_k_grp, 16) || !aligned(a->cb_v_grp, 16))
+      return fail(LOOPVQ_ERR_MISALIGNED, "pool and group-major codebooks must be 16-byte aligned");
   }
   if (cfg->prefix_tokens > 0 && (!a->k_prefix || !a->v_prefix))
     return fail(LOOPVQ_ERR_INVALID_ARG, "prefix windows must not be NULL when prefix_tokens > 0");
@@ -582,8 +603,8 @@ loopvq_status loopvq_extend_attn(const loopvq_config* cfg, const loopvq_extend_a
   p.pool_lj = can_vq ? a->pool + (int64_t(a->layer) * z.J + j) * cfg->num_kv_heads * p.head_stride : nullptr;
   const int64_t set0 = (int64_t(a->layer) * z.Jcb + jcb) * cfg->num_kv_heads;
   const int64_t set_elems = int64_t(cfg->loop_group) * z.K * cfg->head_dim;
-  p.cbk = can_vq ? a->cb_k_prep + set0 * set_elems : nullptr;
-  p.cbv = can_vq ? a->cb_v_prep + set0 * set_elems : nullptr;
+  p.cbk = can_vq ? a->cb_k_grp + set0 * set_elems : nullptr;
+  p.cbv = can_vq ? a->cb_v_grp + set0 * set_elems : nullptr;
   p.k_prefix = a->k_prefix;
   p.v_prefix = a->v_prefix;
   p.k_recent = a->k_recent;

@@ -14,7 +14,9 @@
 //  * each tile is staged in LDS by the whole workgroup: K as [token][d] bf16 rows and V
 //    transposed as [d][token] bf16 (rows padded so the MFMA operand reads hit distinct banks).
 //    Vector-quantized tokens are dequantized on the way: the packed index byte of (token,
-//    group) selects c channels of the loop-step slice of the prepared codebook.
+//    group) selects the c channels of that group's loop-step slice, read from the group-major
+//    codebook copy ([tau][g][k][i]), so a tile's gathers of one group stay within K x c
+//    elements (2 KB at c=4) and share cache lines.
 //  * per wave: S^T = K Q^T on bf16 32x32x16 MFMAs (a rotated q' = R^T q is split into two
 //    bf16 parts, two MFMAs), online softmax in log2 units with the causal mask of the
 //    chunk, then O^T += V^T P^T with P split into two bf16 parts (hi + lo, 2^-16 relative),
@@ -55,8 +57,13 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendParams p) {
   constexpr int KROW = D + 8;         // bf16 per K row (16 B of padding)
   constexpr int KSTEPS = D / 16;      // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;          // 32-channel blocks of O^T
+  // Without a rotation the q operand lives in LDS (each wave reads back only its own rows), which
+  // frees the registers that hold the next tile's keys and values while this one is consumed.
+  constexpr bool QL = !ROT;
+  constexpr int QROW = D + 8;         // bf16 per q row (16 B of padding)
   __shared__ __align__(16) uint16_t ks[kKT * KROW];
   __shared__ __align__(16) uint16_t vt[D * kVRow];
+  __shared__ __align__(16) uint16_t qs[QL ? kRows * QROW : 8];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -110,8 +117,13 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendParams p) {
   } else {
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
-      bq[kk] = *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * half);
-      bq_lo[kk] = u32x4{0u, 0u, 0u, 0u};
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * half);
+      if constexpr (QL) {
+        *reinterpret_cast<u32x4*>(qs + (wave * 32 + col) * QROW + 16 * kk + 8 * half) = v;
+      } else {
+        bq[kk] = v;
+        bq_lo[kk] = u32x4{0u, 0u, 0u, 0u};
+      }
     }
   }
 
@@ -192,8 +204,8 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendParams p) {
         for (int r = 0; r < 4; ++r) {
           const int g = 4 * gq + r;
           const uint32_t kx = (ik[m] >> (8 * r)) & 0xffu, vx = (iv[m] >> (8 * r)) & 0xffu;
-          const uint32_t* kc = reinterpret_cast<const uint32_t*>(slice_k + kx * D + g * C);
-          const uint32_t* vc = reinterpret_cast<const uint32_t*>(slice_v + vx * D + g * C);
+          const uint32_t* kc = reinterpret_cast<const uint32_t*>(slice_k + (g * kCodes + kx) * C);
+          const uint32_t* vc = reinterpret_cast<const uint32_t*>(slice_v + (g * kCodes + vx) * C);
 #pragma unroll
           for (int e = 0; e < C / 2; ++e) {
             fk[(m * 4 + r) * (C / 2) + e] = kc[e];
@@ -278,7 +290,9 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendParams p) {
       f32x16 acc = {};
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[kk]), as_bf16x8(bq[kk]), acc, 0, 0, 0);
+        const u32x4 qb = QL ? *reinterpret_cast<const u32x4*>(qs + (wave * 32 + col) * QROW + 16 * kk + 8 * half)
+                            : bq[kk];
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[kk]), as_bf16x8(qb), acc, 0, 0, 0);
         if constexpr (ROT)
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[kk]), as_bf16x8(bq_lo[kk]), acc, 0, 0, 0);
       }
@@ -357,14 +371,31 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendParams p) {
 
   // ---- the key tiles ------------------------------------------------------------------------------
   fetch_idx(0, ik_n, iv_n, ok_n);
-  for (int k = 0; k < n_tiles; ++k) {
-    fetch(k, ik_n, iv_n, ok_n);
-    if (k + 1 < n_tiles) fetch_idx(k + 1, ik_n, iv_n, ok_n);
-    __syncthreads();                  // every wave is done with the previous tile
-    store(k);
-    __syncthreads();
-    const Tile tl = tile_of(k);
-    consume(tl.count, tl.seg == 3 ? tl.start : -1);
+  if constexpr (QL) {
+    // tile k + 1's keys and values load while tile k is consumed
+    fetch(0, ik_n, iv_n, ok_n);
+    if (1 < n_tiles) fetch_idx(1, ik_n, iv_n, ok_n);
+    for (int k = 0; k < n_tiles; ++k) {
+      __syncthreads();                // every wave is done with the previous tile
+      store(k);
+      __syncthreads();
+      if (k + 1 < n_tiles) {
+        fetch(k + 1, ik_n, iv_n, ok_n);
+        if (k + 2 < n_tiles) fetch_idx(k + 2, ik_n, iv_n, ok_n);
+      }
+      const Tile tl = tile_of(k);
+      consume(tl.count, tl.seg == 3 ? tl.start : -1);
+    }
+  } else {
+    for (int k = 0; k < n_tiles; ++k) {
+      fetch(k, ik_n, iv_n, ok_n);
+      if (k + 1 < n_tiles) fetch_idx(k + 1, ik_n, iv_n, ok_n);
+      __syncthreads();                // every wave is done with the previous tile
+      store(k);
+      __syncthreads();
+      const Tile tl = tile_of(k);
+      consume(tl.count, tl.seg == 3 ? tl.start : -1);
+    }
   }
 
   // ---- normalise and write: O^T register r of block db is channel 32db + 8(r/4) + 4half + r%4

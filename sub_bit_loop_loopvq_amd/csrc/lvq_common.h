@@ -81,7 +81,7 @@ struct ExtendParams {
   const int32_t* chunk_lens; // [B] or nullptr (all M)
   const int32_t* block_table;
   const uint8_t* pool_lj;    // pool + ((l*J + j)*Hkv) * head_stride, or nullptr (no VQ rows)
-  const uint16_t* cbk;       // prepared key codebooks of (l, jcb): [Hkv][G][K][d]
+  const uint16_t* cbk;       // group-major key codebooks of (l, jcb): [Hkv][G][NG][K][c]
   const uint16_t* cbv;
   const uint16_t* k_prefix;  // [B][Hkv][P][d]
   const uint16_t* v_prefix;
@@ -120,6 +120,7 @@ hipError_t launch_decode(const DecodeParams& p, int ng, int c, hipStream_t strea
 hipError_t launch_encode(const EncodeParams& p, int c, hipStream_t stream);
 hipError_t launch_extend(const ExtendParams& p, int ng, int c, hipStream_t stream);
 hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream);
+hipError_t launch_prepare_groups(const PrepareParams& p, hipStream_t stream);
 hipError_t launch_lloyd(const LloydParams& p, int c, hipStream_t stream);
 
 // ---------------------------------------------------------------------------

@@ -25,6 +25,25 @@ __global__ void __launch_bounds__(256) prepare_slices(PrepareParams p) {
   }
 }
 
+// Group-major loop slices for extend: [set][tau][g][k][i].  A gather of one group's channels of
+// codeword k then stays inside that group's K x c block (2 KB at c=4), so the gathers of a tile
+// touch few cache lines.
+__global__ void __launch_bounds__(256) prepare_groups(PrepareParams p) {
+  const int64_t total = p.sets * p.G * p.NG * p.K * p.c;
+  const int E = p.c * p.G;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+    const int i = (int)(idx % p.c);
+    const int64_t r1 = idx / p.c;
+    const int k = (int)(r1 % p.K);
+    const int64_t r2 = r1 / p.K;
+    const int g = (int)(r2 % p.NG);
+    const int64_t r3 = r2 / p.NG;
+    const int tau = (int)(r3 % p.G);
+    const int64_t set = r3 / p.G;
+    p.prep[idx] = p.cb[((set * p.NG + g) * p.K + k) * E + tau * p.c + i];
+  }
+}
+
 __global__ void __launch_bounds__(256) prepare_norms(PrepareParams p) {
   const int64_t total = p.sets * p.NG * p.K;
   const int E = p.c * p.G;
@@ -34,6 +53,13 @@ __global__ void __launch_bounds__(256) prepare_norms(PrepareParams p) {
 }
 
 }  // namespace
+
+hipError_t launch_prepare_groups(const PrepareParams& p, hipStream_t stream) {
+  const int64_t n = p.sets * p.G * p.NG * p.K * p.c;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(prepare_groups, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream) {
   const int64_t n1 = p.sets * p.G * p.K * p.d;

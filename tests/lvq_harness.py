@@ -152,11 +152,13 @@ class Case:
         lay = lvq.loopvq_layout_query(self.cfg, wl.batch, self.paging.num_pages)
         self.lay = lay
         self.d_cb = {0: dev_u16(self.cbk), 1: dev_u16(self.cbv)}
-        self.d_prep, self.d_norm = {}, {}
+        self.d_prep, self.d_norm, self.d_grp = {}, {}, {}
         for kind in (0, 1):
             self.d_prep[kind] = torch.empty_like(self.d_cb[kind])
+            self.d_grp[kind] = torch.empty_like(self.d_cb[kind])
             self.d_norm[kind] = torch.empty(lay.norms_elems, dtype=torch.float32, device=DEV)
             lvq.loopvq_codebook_prepare(self.cfg, self.d_cb[kind], self.d_prep[kind], self.d_norm[kind])
+            lvq.loopvq_codebook_prepare_groups(self.cfg, self.d_cb[kind], self.d_grp[kind])
         self.d_bt = dev_i32(self.paging.table)
         self.d_lens = dev_i32(self.lens)
         self.d_q = dev_u16(self.q)

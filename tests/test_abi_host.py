@@ -230,8 +230,8 @@ def test_evict_needs_a_recent_window_and_a_built_variant():
 
 def _extend_kw(**over):
     kw = dict(layer=0, loop=0, batch=2, chunk=16, q=FAKE, k_new=FAKE, v_new=FAKE, seq_lens=FAKE, max_seq_len=500,
-              out=FAKE, block_table=FAKE, pool=FAKE, max_pages_per_seq=8, num_pages=16, cb_k_prep=FAKE,
-              cb_v_prep=FAKE, k_prefix=FAKE, v_prefix=FAKE, k_recent=FAKE, v_recent=FAKE, stream=0)
+              out=FAKE, block_table=FAKE, pool=FAKE, max_pages_per_seq=8, num_pages=16, cb_k_grp=FAKE,
+              cb_v_grp=FAKE, k_prefix=FAKE, v_prefix=FAKE, k_recent=FAKE, v_recent=FAKE, stream=0)
     kw.update(over)
     return kw
 
@@ -301,6 +301,16 @@ def test_lloyd_workspace_sizes():
         with pytest.raises(lvq.LoopVQError) as e:
             lvq.loopvq_lloyd_step(pg, **_lloyd_kw(cb_set=bad, stride_loop=1000 * 32 * 128, stride_token=32 * 128))
         assert e.value.status == lvq.LOOPVQ_ERR_INVALID_ARG
+
+
+def test_codebook_prepare_groups_rejects():
+    cfg = lvq.make_config(W.TINY)
+    with pytest.raises(lvq.LoopVQError) as e:
+        lvq.loopvq_codebook_prepare_groups(cfg, None, FAKE, stream=0)
+    assert e.value.status == lvq.LOOPVQ_ERR_INVALID_ARG
+    with pytest.raises(lvq.LoopVQError) as e:
+        lvq.loopvq_codebook_prepare_groups(cfg, FAKE, FAKE + 2, stream=0)
+    assert e.value.status == lvq.LOOPVQ_ERR_MISALIGNED
 
 
 def test_codebook_prepare_rejects():

@@ -55,7 +55,7 @@ def test_extend_matches_oracle(name):
                            v_new=H.dev_u16(vn), seq_lens=case.d_lens, max_seq_len=int(max(lens)), out=out,
                            chunk_lens=H.dev_i32(clens) if clens is not None else None, block_table=case.d_bt,
                            pool=case.pool_base(), max_pages_per_seq=case.paging.max_pages,
-                           num_pages=case.paging.num_pages, cb_k_prep=case.d_prep[0], cb_v_prep=case.d_prep[1],
+                           num_pages=case.paging.num_pages, cb_k_grp=case.d_grp[0], cb_v_grp=case.d_grp[1],
                            k_prefix=case.d_win[0], v_prefix=case.d_win[1], k_recent=case.d_win[2],
                            v_recent=case.d_win[3], rot=case.d_rot)
     torch.cuda.synchronize()
@@ -78,3 +78,21 @@ def test_extend_matches_oracle(name):
             worst = (max(worst[0], rel), max(worst[1], mx))
             checked += Mb
     print(f"  {checked} rows checked; worst rel-L2 {worst[0]:.2e}, max-abs {worst[1]:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("c,G,d", [(4, 4, 128), (8, 2, 128), (4, 8, 64)])
+def test_group_major_codebooks_layout(c, G, d):
+    """loopvq_codebook_prepare_groups writes [L][Jcb][Hkv][G][NG][K][c]: the canonical rows
+    [..][NG][K][G*c] with each row split into its G loop slices, moved in front of the groups."""
+    wl = W.TINY.with_(layers=2, loops=2 * G, loop_group=G, chans=c, head_dim=d, kv_heads=2, q_heads=2,
+                      codebook_per_loop_group=True)
+    cfg = lvq.make_config(wl)
+    L, Jcb, Hkv, NG, K = wl.layers, wl.cb_loop_groups, wl.kv_heads, wl.groups, wl.codewords
+    bits = np.random.default_rng(12).integers(0, 1 << 16, size=(L, Jcb, Hkv, NG, K, G * c)).astype(np.uint16)
+    d_cb = H.dev_u16(bits)
+    d_grp = torch.empty_like(d_cb)
+    lvq.loopvq_codebook_prepare_groups(cfg, d_cb, d_grp)
+    torch.cuda.synchronize()
+    want = bits.reshape(L, Jcb, Hkv, NG, K, G, c).transpose(0, 1, 2, 5, 3, 4, 6)
+    got = d_grp.cpu().numpy().view(np.uint16).reshape(want.shape)
+    assert np.array_equal(got, want)
