@@ -547,7 +547,8 @@ loopvq_status loopvq_extend_attn(const loopvq_config* cfg, const loopvq_extend_a
   if (a->batch < 1 || a->chunk < 1) return fail(LOOPVQ_ERR_INVALID_ARG, "batch and chunk must be >= 1");
   if (a->max_seq_len < 0) return fail(LOOPVQ_ERR_INVALID_ARG, "max_seq_len must be >= 0");
   const int grp = cfg->num_q_heads / cfg->num_kv_heads;
-  const int64_t row_blocks = (int64_t(a->chunk) * grp + 127) / 128;
+  const int rows_wg = a->rot ? 128 : 256;   // query rows per workgroup of the kernel variant
+  const int64_t row_blocks = (int64_t(a->chunk) * grp + rows_wg - 1) / rows_wg;
   if (int64_t(a->batch) * cfg->num_kv_heads * row_blocks > (int64_t(1) << 31) - 1)
     return fail(LOOPVQ_ERR_INVALID_ARG, "batch * kv_heads * chunk too large for one launch");
   if (!a->q || !a->k_new || !a->v_new || !a->seq_lens || !a->out)

@@ -35,7 +35,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kKT = 64;        // keys per tile
-constexpr int kRows = 128;     // query rows per workgroup
 constexpr int kVRow = kKT + 4; // bf16 per transposed V row (8 B of padding)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -52,7 +51,11 @@ __device__ __forceinline__ void split2(float v, uint32_t& hi, uint32_t& lo) {
 }
 
 template <int NG, int C, bool ROT>
-__global__ void __launch_bounds__(256, 2) extend_kernel(ExtendParams p) {
+__global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(ExtendParams p) {
+  // Without a rotation: 8 waves (256 query rows) per workgroup, one workgroup per CU, so each
+  // staged tile serves twice the rows; with one, 4 waves and two workgroups per CU.
+  constexpr int NTH = ROT ? 256 : 512;
+  constexpr int kRows = NTH / 2;
   constexpr int D = NG * C;
   constexpr int KROW = D + 8;         // bf16 per K row (16 B of padding)
   constexpr int KSTEPS = D / 16;      // k-steps of S^T = K Q^T
@@ -61,8 +64,11 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendParams p) {
   // frees the registers that hold the next tile's keys and values while this one is consumed.
   constexpr bool QL = !ROT;
   constexpr int QROW = D + 8;         // bf16 per q row (16 B of padding)
-  __shared__ __align__(16) uint16_t ks[kKT * KROW];
-  __shared__ __align__(16) uint16_t vt[D * kVRow];
+  // K / V^T tiles: two buffers without a rotation (tile k + 1 is staged while tile k is consumed)
+  __shared__ __align__(16) uint16_t ks2[QL ? 2 : 1][kKT * KROW];
+  __shared__ __align__(16) uint16_t vt2[QL ? 2 : 1][D * kVRow];
+  uint16_t* ks = ks2[0];
+  uint16_t* vt = vt2[0];
   __shared__ __align__(16) uint16_t qs[QL ? kRows * QROW : 8];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -162,9 +168,11 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendParams p) {
   const uint16_t* v_seg[4] = {p.v_prefix + bhk * p.P * D, nullptr, p.v_recent + bhk * p.R * D, p.v_new + bhk * p.M * D};
 
   constexpr int PIECES = D / 8;                     // 16-byte pieces per bf16 row
-  constexpr int RITEMS = kKT * PIECES / 256;        // row pieces per thread
-  constexpr int QITEMS = kKT * (NG / 4) / 256;      // (token, group quad) items per thread
-  static_assert(RITEMS >= 1 && QITEMS >= 1, "tile mapping");
+  constexpr int RITEMS = kKT * PIECES / NTH;        // row pieces per thread
+  constexpr int QIT = kKT * (NG / 4);               // (token, group quad) items of a tile
+  constexpr int QITEMS = (QIT + NTH - 1) / NTH;     // per thread (the last may be idle)
+  constexpr bool kAllLive = QIT % NTH == 0;
+  static_assert(RITEMS >= 1 && RITEMS * NTH == kKT * PIECES && QITEMS >= 1, "tile mapping");
   constexpr int FB = RITEMS * 4 > QITEMS * 4 * (C / 2) ? RITEMS * 4 : QITEMS * 4 * (C / 2);   // dwords per kind
   uint32_t fk[FB], fv[FB];          // the tile's keys / values on their way to LDS
   uint32_t ik_n[QITEMS], iv_n[QITEMS];   // packed indices of the next tile
@@ -181,9 +189,11 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendParams p) {
     page = pok ? page : 0;
 #pragma unroll
     for (int m = 0; m < QITEMS; ++m) {
-      const int it = tid + 256 * m;
+      const int it0 = tid + NTH * m;
+      const bool live = kAllLive || it0 < QIT;
+      const int it = live ? it0 : 0;
       const int t = it % kKT, gq = it / kKT;
-      ok[m] = pok && t < tl.count;
+      ok[m] = live && pok && t < tl.count;
       const int w = (tl.start + min(t, tl.count - 1)) & pt_mask;
       const uint8_t* tile = pool_h + (int64_t)page * p.page_bytes + (((w >> 2) * (NG / 4) + gq) * 16 + (w & 3) * 4);
       ik[m] = *reinterpret_cast<const uint32_t*>(tile);
@@ -199,7 +209,8 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendParams p) {
 #pragma unroll
       for (int m = 0; m < QITEMS; ++m) {
         ok_cur[m] = ok[m];
-        const int gq = (tid + 256 * m) / kKT;
+        const int it0 = tid + NTH * m;
+        const int gq = (kAllLive || it0 < QIT ? it0 : 0) / kKT;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int g = 4 * gq + r;
@@ -218,7 +229,7 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendParams p) {
       const uint16_t* vw = (tl.seg == 0 ? v_seg[0] : tl.seg == 2 ? v_seg[2] : v_seg[3]) + (int64_t)tl.start * D;
 #pragma unroll
       for (int m = 0; m < RITEMS; ++m) {
-        const int it = tid + 256 * m;
+        const int it = tid + NTH * m;
         const int t = min(it / PIECES, tl.count - 1), pc = it % PIECES;
         const u32x4 kv = *reinterpret_cast<const u32x4*>(kw + (int64_t)t * D + 8 * pc);
         const u32x4 vv = *reinterpret_cast<const u32x4*>(vw + (int64_t)t * D + 8 * pc);
@@ -237,7 +248,8 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendParams p) {
     if (tl.seg == 1) {
 #pragma unroll
       for (int m = 0; m < QITEMS; ++m) {
-        const int it = tid + 256 * m;
+        const int it = tid + NTH * m;
+        if (!kAllLive && it >= QIT) continue;
         const int t = it % kKT, gq = it / kKT;
         const uint32_t keep = ok_cur[m] ? 0xffffffffu : 0u;
 #pragma unroll
@@ -256,7 +268,7 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendParams p) {
     } else {
 #pragma unroll
       for (int m = 0; m < RITEMS; ++m) {
-        const int it = tid + 256 * m;
+        const int it = tid + NTH * m;
         const int t = it / PIECES, pc = it % PIECES;
         const uint32_t keep = t < tl.count ? 0xffffffffu : 0u;
         *reinterpret_cast<u32x4*>(ks + t * KROW + 8 * pc) =
@@ -373,16 +385,28 @@ __global__ void __launch_bounds__(256, 2) extend_kernel(ExtendParams p) {
   fetch_idx(0, ik_n, iv_n, ok_n);
   if constexpr (QL) {
     // tile k + 1's keys and values load while tile k is consumed
+    // two LDS buffers: tile k + 1 is stored, and tile k + 2 loaded into registers, while tile k
+    // is consumed; one barrier per tile
     fetch(0, ik_n, iv_n, ok_n);
     if (1 < n_tiles) fetch_idx(1, ik_n, iv_n, ok_n);
+    store(0);
+    if (1 < n_tiles) {
+      fetch(1, ik_n, iv_n, ok_n);
+      if (2 < n_tiles) fetch_idx(2, ik_n, iv_n, ok_n);
+    }
     for (int k = 0; k < n_tiles; ++k) {
-      __syncthreads();                // every wave is done with the previous tile
-      store(k);
-      __syncthreads();
+      __syncthreads();                // tile k is staged; every wave is done with tile k - 1
       if (k + 1 < n_tiles) {
-        fetch(k + 1, ik_n, iv_n, ok_n);
-        if (k + 2 < n_tiles) fetch_idx(k + 2, ik_n, iv_n, ok_n);
+        ks = ks2[(k + 1) & 1];
+        vt = vt2[(k + 1) & 1];
+        store(k + 1);
+        if (k + 2 < n_tiles) {
+          fetch(k + 2, ik_n, iv_n, ok_n);
+          if (k + 3 < n_tiles) fetch_idx(k + 3, ik_n, iv_n, ok_n);
+        }
       }
+      ks = ks2[k & 1];
+      vt = vt2[k & 1];
       const Tile tl = tile_of(k);
       consume(tl.count, tl.seg == 3 ? tl.start : -1);
     }
@@ -420,9 +444,9 @@ template <int NG, int C>
 hipError_t launch_extend_variant(const ExtendParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.B * p.Hkv * p.row_blocks));
   if (p.rot)
-    hipLaunchKernelGGL((extend_kernel<NG, C, true>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((extend_kernel<NG, C, true>), grid, dim3(256), 0, stream, p);   // 128 rows
   else
-    hipLaunchKernelGGL((extend_kernel<NG, C, false>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((extend_kernel<NG, C, false>), grid, dim3(512), 0, stream, p);  // 256 rows
   return hipGetLastError();
 }
 

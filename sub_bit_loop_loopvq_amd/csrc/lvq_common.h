@@ -69,7 +69,7 @@ struct EncodeParams {
 struct ExtendParams {
   int B, Hq, Hkv, P, R, G;
   int M;                     // chunk rows per sequence (q, k_new, v_new, out stride)
-  int row_blocks;            // workgroups per (sequence, kv-head): ceil(M * Hq/Hkv / 128)
+  int row_blocks;            // workgroups per (sequence, kv-head): ceil(M * Hq/Hkv / rows), 256 rows (128 with a rotation)
   int pt_shift, max_pages, max_seq_len;
   int tau;                   // loop step within its group (t mod G)
   int64_t num_pages, page_bytes, kind_bytes, head_stride;

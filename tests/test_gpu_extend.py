@@ -26,6 +26,10 @@ CASES = {
     # d=128, c=8, rotated keys (q' = R^T q on the GPU)
     "c8_rot": (W.QUARTER_16K.with_(layers=1, batch=2, q_heads=2, kv_heads=2, context=500), 0, 3, [400, 150], 40,
                None),
+    # c=8 without a rotation (16 groups: half of the threads idle in index staging), 300 chunk rows
+    # of GQA 4:1 = 1200 query rows: five 256-row workgroups per (sequence, kv-head), the last ragged
+    "c8_gqa": (W.QUARTER_16K.with_(layers=1, batch=2, q_heads=8, kv_heads=2, context=700, rotate_keys=False), 0, 2,
+               [650, 100], 300, [300, 77]),
     # c=4 over G=8 loop steps (0.25 bit), loop step 6 of its group
     "c4_g8": (W.LAYER_4K.with_(loops=8, loop_group=8, batch=2, q_heads=4, kv_heads=2, context=400), 0, 6, [300, 90],
               50, None),
