@@ -86,28 +86,42 @@ __global__ void __launch_bounds__(1024, 1) lloyd_sums(LloydParams p) {
 #pragma unroll
   for (int gl = 0; gl < GPL; ++gl) dpart[gl] = 0.0;
 
-  for (int64_t rb = r_begin + (threadIdx.x >> 3); rb < r_end; rb += 128 * U) {
+  // rows of one batch: U rows per lane, 128 rows apart; the next batch is loaded while this one's
+  // atomic adds run
+  struct Batch {
     uint4 xv[U];
     int kk[U][GPL];
     float ww[U][GPL];
+  };
+  auto load_batch = [&](int64_t rb, int64_t rvalid, Batch& bt) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t r = rb + u * 128;
-      const int64_t rr = r < r_end ? r : rb;   // a tail lane reloads its first row with weight 0
-      xv[u] = *(const uint4*)(xb + rr * p.stride_token);
+      const int64_t rr = r < r_end ? r : rvalid;   // rows past the end reload a valid row with weight 0
+      bt.xv[u] = *(const uint4*)(xb + rr * p.stride_token);
       const int64_t o = (rr * p.Hkv + h) * p.NG + g0;
       if constexpr (GPL == 2) {
         const int2 k2 = *(const int2*)(p.assign + o);
         const float2 w2 = *(const float2*)(p.weight + o);
-        kk[u][0] = k2.x & (kCodesL - 1);
-        kk[u][1] = k2.y & (kCodesL - 1);
-        ww[u][0] = r < r_end ? w2.x : 0.f;
-        ww[u][1] = r < r_end ? w2.y : 0.f;
+        bt.kk[u][0] = k2.x & (kCodesL - 1);
+        bt.kk[u][1] = k2.y & (kCodesL - 1);
+        bt.ww[u][0] = r < r_end ? w2.x : 0.f;
+        bt.ww[u][1] = r < r_end ? w2.y : 0.f;
       } else {
-        kk[u][0] = p.assign[o] & (kCodesL - 1);
-        ww[u][0] = r < r_end ? p.weight[o] : 0.f;
+        bt.kk[u][0] = p.assign[o] & (kCodesL - 1);
+        bt.ww[u][0] = r < r_end ? p.weight[o] : 0.f;
       }
     }
+  };
+  const int64_t rb0 = r_begin + (threadIdx.x >> 3);
+  Batch cur;
+  if (rb0 < r_end) load_batch(rb0, rb0, cur);
+  for (int64_t rb = rb0; rb < r_end; rb += 128 * U) {
+    Batch nxt;
+    load_batch(rb + 128 * U, rb, nxt);
+    const uint4* xv = cur.xv;
+    int (&kk)[U][GPL] = cur.kk;
+    float (&ww)[U][GPL] = cur.ww;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t xw[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
@@ -154,6 +168,7 @@ __global__ void __launch_bounds__(1024, 1) lloyd_sums(LloydParams p) {
         atomicAdd(&acc[k * kSliceCh + sub * 8 + e], (double)w * (double)xf);
       }
     }
+    cur = nxt;
   }
   if constexpr (DIST) {
 #pragma unroll
