@@ -13,18 +13,18 @@
 //    read their rows directly; bulk encodes give a workgroup all groups of 128 rows and
 //    stage the rows in LDS, 64 channels at a time, with coalesced LDS-direct loads, so that
 //    every cache line is read from HBM once.
-//  * screen: F_k = x.C_k - (||C_k||^2 + ||x||^2) / 2 = -D_k / 2 for a 32-codeword x
-//    32-row tile is two bf16 32x32x16 MFMAs: the first seeds the accumulator with the two
-//    halved squared norms (each split exactly into three bf16 parts), the second adds
-//    C . x on the raw bf16 operands.  Each lane holds 128 of its row's 256 values.
-//  * epilogue: each value is packed with its codeword index in the low 8 mantissa bits;
-//    the two largest packed keys (the two smallest distances) are kept with max3, med3
-//    and max over pairs of keys: 2.5 VALU ops per distance.  The two half-waves that
-//    share a row are merged.
-//  * exactness: the screen errs by at most delta = 2^-16 (||x||^2 + max_k ||C_k||^2) in
-//    distance and the packing truncates by at most 2^-15 relative.  If the two smallest
-//    distances are further apart than both bounds allow, the screened winner is the
-//    exact argmin.  Otherwise (about one row in a thousand) the whole wave scores that row
+//  * screen: S_k = ||C_k||^2 - 2 x.C_k = D_k - ||x||^2 (same order as D_k over k) for a
+//    32-codeword x 32-row tile is one bf16 32x32x16 MFMA per 16 elements: the fp32
+//    squared codeword norms enter as the accumulator input and the B operand is -2x
+//    (exact in bf16).  Each lane holds 128 of its row's 256 values.
+//  * epilogue: each value is packed with its index among the lane's 128 codewords in the
+//    low 7 mantissa bits; the two smallest packed keys are kept with min3, med3 and min
+//    over pairs of keys: 2.5 VALU ops per distance.  The two half-waves that share a row
+//    are merged.
+//  * exactness: the screen errs by at most delta = 2^-18 (||x||^2 + max_k ||C_k||^2) in
+//    distance at 16 elements (2^-17 at 32) and the packing truncates by at most 2^-16
+//    relative.  If the two smallest screened values are further apart than both bounds
+//    allow, the screened winner is the exact argmin.  Otherwise (about one row in a thousand) the whole wave scores that row
 //    against all 256 codewords as sequential fp64 sums of squared differences and keeps
 //    the lowest exact minimiser (the brute-force definition).
 //  * packing: the 8-bit index is stored as one byte of its 16-index micro-tile
@@ -35,23 +35,44 @@ namespace lvq {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(1))) void global_void;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// v -> (hi, mid, lo) bf16 parts with hi + mid + lo == v to within 2^-24 |v| (truncating splits)
-__device__ __forceinline__ void split3(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-  const uint32_t b0 = __float_as_uint(v) & 0xffff0000u;
-  const float r1 = v - __uint_as_float(b0);
-  const uint32_t b1 = __float_as_uint(r1) & 0xffff0000u;
-  const float r2 = r1 - __uint_as_float(b1);
-  const uint32_t b2 = __float_as_uint(r2) & 0xffff0000u;
-  hi = b0 >> 16;
-  mid = b1 >> 16;
-  lo = b2 >> 16;
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// -2 times two packed finite bf16, exactly: doubling a 15-bit magnitude m adds one to the
+// exponent field (m + 0x80) when it is nonzero and doubles m when it is zero (a subnormal or
+// zero, where m < 0x80), i.e. adds min(m, 0x80); no half carries into the next for finite
+// values.  The sign flips.
+__device__ __forceinline__ uint32_t neg2_bf16x2(uint32_t w) {
+  const u16x2 inc = __builtin_elementwise_min(__builtin_bit_cast(u16x2, w & 0x7fff7fffu), u16x2{0x80, 0x80});
+  return (w ^ 0x80008000u) + __builtin_bit_cast(uint32_t, inc);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+// (value of half 0, value of half 1) of a wave register, in every lane
+__device__ __forceinline__ void halves(uint32_t v, uint32_t& h0, uint32_t& h1) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  h0 = r[0];
+  h1 = r[1];
+}
+
+// maximum over the wave without LDS: quad, half-row and row mirrors, then the row pairs and
+// the wave halves
+__device__ __forceinline__ float wave_max_nolds(float v) {
+  v = fmaxf(v, dpp<0xb1>(v));    // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp<0x4e>(v));    // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp<0x140>(v));   // row_mirror
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  uint32_t h0, h1;
+  halves(__float_as_uint(v), h0, h1);
+  return fmaxf(__uint_as_float(h0), __uint_as_float(h1));
+}
 
 // value of a packed key with its index bits cleared
 __device__ __forceinline__ float key_value(float k) { return __uint_as_float(__float_as_uint(k) & 0xffffff00u); }
@@ -77,6 +98,7 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
   constexpr int E = G * C;        // sub-vector length (16 or 32)
   constexpr int NMF = E / 16;     // code MFMAs per distance tile
   constexpr int ROWS = 32 * TT;   // rows of the block
+  constexpr float kDelta = E == 16 ? 0x1p-18f : 0x1p-17f;   // >= 3E 2^-24
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -112,7 +134,6 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
     return o;
   };
   const int pt_mask = (1 << p.pt_shift) - 1;
-  const uint32_t one2 = 0x3f803f80u;   // two bf16 ones
   __shared__ __align__(16) uint8_t stage[STAGE ? G * ROWS * 128 : 16];
   // rows whose screen is not conclusive, as (row in block) * 32 + group, re-ranked exactly
   // after the screen so that no wave holds up the others in the middle of it
@@ -173,19 +194,19 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
   auto nrm_rsrc_of = [&](int gq) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)(nrm_h + gq * kCodes), (short)0, kCodes * 4, kRawBufferWord3);
   };
-  // A operand rows ct*32 + col of a code tile (elements [16m + 8*half, +8)) and the squared
-  // norm of codeword ct*32 + col
-  auto fetch_code = [&](__amdgpu_buffer_rsrc_t cr, __amdgpu_buffer_rsrc_t nr, int ct, u32x4* a, float& nv) {
+  // A operand rows ct*32 + col of a code tile (elements [16m + 8*half, +8)) and the tile's
+  // accumulator input: register r of lane (col, half) holds the squared norm of codeword
+  // ct*32 + 8*(r/4) + 4*half + r%4, the output row the 32x32 MFMA gives it
+  auto fetch_code = [&](__amdgpu_buffer_rsrc_t cr, __amdgpu_buffer_rsrc_t nr, int ct, u32x4* a, f32x16& cn16) {
 #pragma unroll
     for (int m = 0; m < NMF; ++m)
       a[m] = __builtin_amdgcn_raw_buffer_load_b128(cr, ((ct * 32 + col) * E + 16 * m + 8 * half) * 2, 0, 0);
-    nv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(nr, (ct * 32 + col) * 4, 0, 0));
-  };
-  // A operand of the norm MFMA: [-|C|^2/2 in three parts, 1, 1, 1, 0, 0] in half 0, zero in half 1
-  auto norm_operand = [&](float nv) -> u32x4 {
-    uint32_t nh, nm, nl;
-    split3(-0.5f * nv, nh, nm, nl);
-    return half == 0 ? u32x4{nh | (nm << 16), nl | (0x3f80u << 16), one2, 0u} : u32x4{0u, 0u, 0u, 0u};
+    u32x4 q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = __builtin_amdgcn_raw_buffer_load_b128(nr, (ct * 32 + 8 * i + 4 * half) * 4, 0, 0);
+    cn16 = __builtin_bit_cast(f32x16, __builtin_shufflevector(__builtin_shufflevector(q[0], q[1], 0, 1, 2, 3, 4, 5, 6, 7),
+                                                              __builtin_shufflevector(q[2], q[3], 0, 1, 2, 3, 4, 5, 6, 7),
+                                                              0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15));
   };
   // raw sub-vector elements [16m + 8*half, +8) of each tile's row col for group gq (direct
   // loads read the last row for rows past the end; such rows are zeroed where used)
@@ -264,9 +285,11 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
   };
 
   const int gend = min(g0 + groups_per_wg, NG);
-  u32x4 a_first[NMF];      // first code tile of the group about to be screened
-  float n_first;
-  if (g0 + wave < gend) fetch_code(cb_rsrc_of(g0 + wave), nrm_rsrc_of(g0 + wave), 0, a_first, n_first);
+  // code tiles in flight: even tiles in A, odd tiles in B (no register copies between
+  // tiles); A receives the next group's first tile during the current group's last tile
+  u32x4 aA[NMF], aB[NMF];
+  f32x16 nA, nB;
+  if (g0 + wave < gend) fetch_code(cb_rsrc_of(g0 + wave), nrm_rsrc_of(g0 + wave), 0, aA, nA);
 
   // (a bulk workgroup owns all groups, so every wave passes the same staging barriers)
   for (int g = g0 + wave; g < gend; g += 4) {
@@ -282,141 +305,129 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
       }
     }
 
-    // ---- operands of this group's rows ----
-    u32x4 xb[TT][NMF];             // x, the B operand of the code MFMAs
-    u32x4 bn[TT];                  // B operand of the norm MFMA: [1, 1, 1, -|x|^2/2 in three parts, 0, 0]
-    float xn[TT];                  // |x|^2
-    float cn[4];
+    // ---- operands of this group's rows (rows past the end hold the last row's values and
+    //      are neither stored nor re-ranked) ----
+    u32x4 xb[TT][NMF];             // -2x, the B operand of the code MFMAs
+    float xn[TT];                  // |x|^2 (it only enters the screen's error bound)
+    float cn[4];                   // used after the screen: the loads are in flight meanwhile
     fetch_rows(g, xb);
     fetch_cnorms(g, cn);
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
-      const bool ok = row0 + tt * 32 + col < p.n_tokens;
       float nn = 0.f;
 #pragma unroll
-      for (int m = 0; m < NMF; ++m) {
-        if (!ok) xb[tt][m] = u32x4{0u, 0u, 0u, 0u};
+      for (int m = 0; m < NMF; ++m)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const float a = bf16_lo(xb[tt][m][w]), b = bf16_hi(xb[tt][m][w]);
-          nn = fmaf(a, a, nn);
-          nn = fmaf(b, b, nn);
+          nn = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xb[tt][m][w]),
+                                               __builtin_bit_cast(bf16x2, xb[tt][m][w]), nn, false);
+          xb[tt][m][w] = neg2_bf16x2(xb[tt][m][w]);
         }
-      }
-      nn += __shfl_xor(nn, 32, 64);
-      xn[tt] = nn;
-      uint32_t xh, xm, xl;
-      split3(-0.5f * nn, xh, xm, xl);
-      bn[tt] = half == 0 ? u32x4{one2, 0x3f80u | (xh << 16), xm | (xl << 16), 0u} : u32x4{0u, 0u, 0u, 0u};
+      uint32_t n0, n1;
+      halves(__float_as_uint(nn), n0, n1);
+      xn[tt] = __uint_as_float(n0) + __uint_as_float(n1);
     }
-    // largest squared codeword norm of this group (for the screen's error bound)
-    const float cmax = wave_max(fmaxf(fmaxf(cn[0], cn[1]), fmaxf(cn[2], cn[3])));
 
-    auto screen = [&](const u32x4* a, const u32x4& an, const u32x4* xs, const u32x4& bs) -> f32x16 {
-      f32x16 acc = {};
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(an), as_bf16x8(bs), acc, 0, 0, 0);
+    auto screen = [&](const u32x4* a, const f32x16& cn16, const u32x4* xs) -> f32x16 {
+      f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[0]), as_bf16x8(xs[0]), cn16, 0, 0, 0);
 #pragma unroll
-      for (int m = 0; m < NMF; ++m)
+      for (int m = 1; m < NMF; ++m)
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[m]), as_bf16x8(xs[m]), acc, 0, 0, 0);
       return acc;
     };
 
-    // ---- screen: 8 tiles of 32 codewords; keep the two largest packed keys per lane ----
-    // key = F bits with the low 8 mantissa bits replaced by the index within the lane's
-    // codeword set (k = local + 4 * half).  F is at most 0 up to rounding, so a larger key
-    // holds a smaller distance and, on equal F, a smaller index.  Keys are taken two at a
-    // time: the new maximum is max3(b1, k0, k1) and the new second maximum is
-    // max(b2, med3(b1, k0, k1)) (if b2 stays among the two largest, b1 is the largest and
-    // both keys are <= b2; otherwise the two largest are among b1, k0, k1 and med3 is the
-    // smaller of them).  Keys are finite and never NaN, so no canonicalisation is needed.
+    // ---- screen: 8 tiles of 32 codewords; keep the two smallest packed keys per lane ----
+    // key = S bits with the low 7 mantissa bits replaced by the index j = 16 ct + r of the
+    // value within the lane's 128 codewords (register r of tile ct holds codeword
+    // 32 ct + 8 (r / 4) + 4 half + r % 4).  Clearing low mantissa bits moves a value towards
+    // zero, which keeps the order of distinct truncated values; keys with equal truncated
+    // values are never told apart without the exact re-rank.  Keys are taken two at a time:
+    // the new minimum is min3(b1, k0, k1) and the new second minimum is min(b2, med3(b1, k0,
+    // k1)) (if b2 stays among the two smallest, b1 is the smallest and both keys are >= b2;
+    // otherwise the two smallest are among b1, k0, k1 and med3 is the larger of them).  Keys
+    // are finite and never NaN, so no canonicalisation is needed.
     float b1[TT], b2[TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
-      b1[tt] = -INFINITY;
-      b2[tt] = -INFINITY;
+      b1[tt] = INFINITY;
+      b2[tt] = INFINITY;
     }
     // the key mask in a register (as a literal it would split each pack into two ops)
     uint32_t keep;
-    asm("v_mov_b32 %0, %1" : "=v"(keep) : "s"(0xffffff00u));
+    asm("v_mov_b32 %0, %1" : "=v"(keep) : "s"(0xffffff80u));
     auto consume = [&](const f32x16 (&acc)[TT], int ct) {
       // first index of the tile, hidden from the optimiser: with known low bits it would
       // split each pack into an and plus an add
       uint32_t ctb;
-      asm("s_mov_b32 %0, %1" : "=s"(ctb) : "s"(ct * 32));
+      asm("s_mov_b32 %0, %1" : "=s"(ctb) : "s"(ct * 16));
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           // index of register r in this lane's codeword set
-          const uint32_t kl = ctb + 8 * (r >> 2) + (r & 3);
+          const uint32_t kl = ctb + r;
           const float k0 = __uint_as_float((__float_as_uint(acc[tt][r]) & keep) | kl);
           const float k1 = __uint_as_float((__float_as_uint(acc[tt][r + 1]) & keep) | (kl + 1));
           // (plain VALU operands only: the MFMA results are read by the compiled pack above,
           // whose wait states the compiler inserts)
           float t;
           asm("v_med3_f32 %2, %0, %3, %4\n\t"
-              "v_max3_f32 %0, %0, %3, %4\n\t"
-              "v_max_f32 %1, %1, %2"
+              "v_min3_f32 %0, %0, %3, %4\n\t"
+              "v_min_f32 %1, %1, %2"
               : "+v"(b1[tt]), "+v"(b2[tt]), "=&v"(t)
               : "v"(k0), "v"(k1));
         }
       }
     };
-    u32x4 a_cur[NMF];
-    float n_cur = n_first;
-#pragma unroll
-    for (int m = 0; m < NMF; ++m) a_cur[m] = a_first[m];
 #pragma unroll 1
-    for (int ct = 0; ct < kCodes / 32 - 1; ++ct) {
-      u32x4 a_nxt[NMF];
-      float n_nxt;
-      fetch_code(cb_rsrc, nrm_rsrc, ct + 1, a_nxt, n_nxt);
-      const u32x4 an_cur = norm_operand(n_cur);
-      f32x16 acc[TT];
+    for (int ct = 0; ct < kCodes / 32; ct += 2) {
+      fetch_code(cb_rsrc, nrm_rsrc, ct + 1, aB, nB);
+      {
+        f32x16 acc[TT];
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) acc[tt] = screen(a_cur, an_cur, xb[tt], bn[tt]);
-      consume(acc, ct);
+        for (int tt = 0; tt < TT; ++tt) acc[tt] = screen(aA, nA, xb[tt]);
+        consume(acc, ct);
+        // the tile after next, or the next group's first tile (this group's first after the
+        // last group), arrives while tile ct + 1 is finished.  The load is unconditional, so
+        // that the wait before tile ct + 1 counts only the loads of B.
+        const bool more = ct + 2 < kCodes / 32;
+        const bool next_g = !more && g + 4 < gend;
+        fetch_code(more ? cb_rsrc : (next_g ? cb_rsrc_of(g + 4) : cb_rsrc),
+                   more ? nrm_rsrc : (next_g ? nrm_rsrc_of(g + 4) : nrm_rsrc), more ? ct + 2 : 0, aA, nA);
+      }
+      {
+        f32x16 acc[TT];
 #pragma unroll
-      for (int m = 0; m < NMF; ++m) a_cur[m] = a_nxt[m];
-      n_cur = n_nxt;
-    }
-    {
-      // last tile: its products are issued first, then the next group's first code tile is
-      // fetched so that it arrives while this group is finished
-      const u32x4 an_cur = norm_operand(n_cur);
-      f32x16 acc[TT];
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) acc[tt] = screen(a_cur, an_cur, xb[tt], bn[tt]);
-      if (g + 4 < gend) fetch_code(cb_rsrc_of(g + 4), nrm_rsrc_of(g + 4), 0, a_first, n_first);
-      consume(acc, kCodes / 32 - 1);
+        for (int tt = 0; tt < TT; ++tt) acc[tt] = screen(aB, nB, xb[tt]);
+        consume(acc, ct + 1);
+      }
     }
 
     // ---- merge the two half-waves and decide ----
+    // largest squared codeword norm of this group (for the screen's error bound)
+    const float cmax = wave_max_nolds(fmaxf(fmaxf(cn[0], cn[1]), fmaxf(cn[2], cn[3])));
     uint32_t best[TT];
     bool rerank[TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       const bool ok = row0 + tt * 32 + col < p.n_tokens;
-      // the lane's own keys carry local indices; make them global (k = local + 4*half)
-      const float ob1 = __shfl_xor(b1[tt], 32, 64);
-      const float ob2 = __shfl_xor(b2[tt], 32, 64);
-      const uint32_t myk = (__float_as_uint(b1[tt]) & 0xffu) + 4u * half;
-      const uint32_t ok1 = (__float_as_uint(ob1) & 0xffu) + 4u * (half ^ 1);
-      const float v1 = key_value(b1[tt]), w1 = key_value(ob1);
-      float f1, f2;
-      uint32_t k1;
-      if (w1 > v1 || (w1 == v1 && ok1 < myk)) {
-        f1 = w1;
-        k1 = ok1;
-        f2 = fmaxf(v1, key_value(ob2));
-      } else {
-        f1 = v1;
-        k1 = myk;
-        f2 = fmaxf(key_value(b2[tt]), w1);
-      }
-      const float d1 = -2.f * f1, d2 = -2.f * f2;                            // screened distances
-      const float delta = 7.62939453125e-06f * (xn[tt] + cmax);              // 2^-17 (|x|^2 + max|C|^2)
-      const float trunc = 6.103515625e-05f * fmaxf(fabsf(d1), fabsf(d2));    // 2^-14 max(|d1|, |d2|)
+      // both halves' two smallest keys in every lane (codeword = local index + 4 * half);
+      // where the smallest truncated values are equal, either index may be taken: the gap is
+      // then zero and the row is re-ranked
+      uint32_t p1, q1, p2, q2;
+      halves(__float_as_uint(b1[tt]), p1, q1);
+      halves(__float_as_uint(b2[tt]), p2, q2);
+      const float u1 = key_value(__uint_as_float(p1)), w1 = key_value(__uint_as_float(q1));
+      const float u2 = key_value(__uint_as_float(p2)), w2 = key_value(__uint_as_float(q2));
+      const uint32_t j1 = w1 < u1 ? q1 & 0x7fu : p1 & 0x7fu;
+      const uint32_t k1 = ((j1 & ~3u) << 1) + (j1 & 3u) + (w1 < u1 ? 4u : 0u);
+      const float d1 = fminf(u1, w1);                                        // screened D - |x|^2
+      const float d2 = fminf(fmaxf(u1, w1), fminf(u2, w2));                  // runner-up
+      // screen error bound: with sequential fp32 sums, E roundings in the products' sum
+      // (whose terms total at most |x|^2 + 2|C|^2) and E - 1 in the codeword norm, i.e. at
+      // most 3E 2^-24 (|x|^2 + |C|^2); 2^-100 covers flushed subnormal products
+      const float delta = kDelta * (xn[tt] + cmax) + 0x1p-100f;
+      const float trunc = 0x1p-15f * fmaxf(fabsf(d1), fabsf(d2));   // two keys, 2^-16 each
       rerank[tt] = ok && !(d2 - d1 > 2.f * delta + trunc);
       best[tt] = k1;
     }
@@ -460,20 +471,22 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
       for (int i = 0; i < C / 2; ++i) xw[t * (C / 2) + i] = xs[i];
     }
     const uint16_t* cb_q = cb_h + (int64_t)gq * kCodes * E;
+    // the lane's four codewords lane + 64 i, loaded together; four independent sums
+    u32x4 cv[kCodes / 64][E / 8];
+#pragma unroll
+    for (int i = 0; i < kCodes / 64; ++i)
+#pragma unroll
+      for (int e8 = 0; e8 < E / 8; ++e8) cv[i][e8] = reinterpret_cast<const u32x4*>(cb_q + (lane + 64 * i) * E)[e8];
     double bd = INFINITY;
     uint32_t bk = 0u;
-#pragma unroll 1
-    for (int i = 0; i < kCodes / 64; ++i) {
-      const uint32_t k = (uint32_t)(lane + 64 * i);
-      u32x4 cv[E / 8];
 #pragma unroll
-      for (int e8 = 0; e8 < E / 8; ++e8) cv[e8] = reinterpret_cast<const u32x4*>(cb_q + k * E)[e8];
+    for (int i = 0; i < kCodes / 64; ++i) {
       double dd = 0.0;
       {
 #pragma clang fp contract(off)
 #pragma unroll
         for (int e2 = 0; e2 < E / 2; ++e2) {
-          const uint32_t cw = cv[e2 >> 2][e2 & 3];
+          const uint32_t cw = cv[i][e2 >> 2][e2 & 3];
           const double d0 = (double)bf16_lo(xw[e2]) - (double)bf16_lo(cw);
           dd = dd + d0 * d0;
           const double d1 = (double)bf16_hi(xw[e2]) - (double)bf16_hi(cw);
@@ -482,7 +495,7 @@ __global__ void __launch_bounds__(256, 2) encode_kernel(EncodeParams p, int grou
       }
       if (dd < bd) {   // k grows with i: a strict comparison keeps the lowest index
         bd = dd;
-        bk = k;
+        bk = (uint32_t)(lane + 64 * i);
       }
     }
     // wave minimum of (distance, index)
