@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "VQ decode-attn queries/s + effective HBM GB/s (% peak), 32K ctx, 0.5 bit/elem"
+BF16_METRIC = "bf16-cache decode-attn queries/s + effective HBM GB/s (% peak), same kernel, 32K ctx"
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "stack24x4_h16_d128_b64_n32k"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stack32k_traffic.md")
@@ -45,7 +46,7 @@ def algorithmic_bytes(wl) -> dict:
     B, H, Hq, d, c = wl.batch, wl.kv_heads, wl.q_heads, wl.head_dim, wl.chans
     idx = B * H * wl.n_vq * (d // c) * (wl.index_bits / 8) * 2
     window = B * H * min(wl.context, wl.prefix + wl.recent) * d * 2 * 2
-    slices = H * (d // c) * wl.codewords * c * 2 * 2
+    slices = H * (d // c) * wl.codewords * c * 2 * 2 if wl.n_vq > 0 else 0   # read only with VQ rows
     qo = B * Hq * d * (2 + 4)
     rot = d * d * 4 if wl.rotate_keys else 0
     return {"idx": idx, "window": window, "slices": slices, "q_out": qo, "rot": rot,
@@ -261,6 +262,67 @@ class MixedBench:
             e1 = E(enable_timing=True)
             e1.record()
             evict_events.append((e0, e1))
+
+
+class Bf16Bench:
+    """The same decode kernel over an uncompressed bf16 cache: the recent window covers the whole
+    context (recent = context - prefix), so no token is vector-quantized and every launch streams
+    bf16 K and V rows.  The bf16 cache of the whole stack would not fit in HBM (1.65 TB at the 32K
+    workload), so one (layer, loop step) window pair is generated and every launch of the step
+    reads it; each launch still streams its full bytes from HBM (17.2 GB per launch, far beyond
+    the 256 MB Infinity Cache)."""
+
+    def __init__(self, wl):
+        import torch
+        import sub_bit_loop_loopvq_amd as lvq
+        from synth import gen
+        from synth.device import DeviceGen
+        self.torch, self.lvq = torch, lvq
+        wl = wl.with_(name=wl.name + "_bf16", recent=wl.context - wl.prefix)
+        self.wl = wl
+        dev = "cuda"
+        L, T = wl.layers, wl.loops
+        B, H, d, P, R = wl.batch, wl.kv_heads, wl.head_dim, wl.prefix, wl.recent
+        self.cfg = lvq.make_config(wl)
+        t0 = time.time()
+        q = np.stack([np.stack([gen.queries(wl, l, t) for t in range(T)]) for l in range(L)])
+        self.q = torch.from_numpy(q.view(np.int16)).to(dev)                  # [L][T][B][Hq][d]
+        self.rot = (torch.from_numpy(gen.rotation_matrix_f32(wl)).to(dev) if wl.rotate_keys else None)
+        self.lens = torch.full((B,), wl.context, dtype=torch.int32, device=dev)
+        dg = DeviceGen(wl)
+        self.pre = torch.empty((2, B, H, P, d), dtype=torch.int16, device=dev)
+        self.rec = torch.empty((2, B, H, R, d), dtype=torch.int16, device=dev)
+        for kind in (0, 1):
+            dg.kv(self.pre[kind], kind=kind, layer=0, b0=0, nb=B, h0=0, nh=H, n0=0, nn=P, t0=0, nt=1,
+                  s_loop=B * H * P * d, s_b=H * P * d, s_h=P * d, s_n=d)
+            dg.kv(self.rec[kind], kind=kind, layer=0, b0=0, nb=B, h0=0, nh=H, n0=P, nn=R, t0=0, nt=1,
+                  s_loop=B * H * R * d, s_b=H * R * d, s_h=R * d, s_n=d)
+        torch.cuda.synchronize()
+        self.ws_bytes = lvq.loopvq_decode_attn_workspace(self.cfg, B, wl.context)
+        self.ws = torch.empty(max(16, self.ws_bytes), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((B, wl.q_heads, d), dtype=torch.float32, device=dev)
+        self.setup_s = time.time() - t0
+        log(f"bf16 windows ready ({self.setup_s:.1f}s): {self.rec.numel() * 2 / 1e9:.1f} GB")
+
+    def decode(self, l, t):
+        wl = self.wl
+        self.lvq.loopvq_decode_attn(
+            self.cfg, layer=l, loop=t, batch=wl.batch, q=self.q[l, t], seq_lens=self.lens, max_seq_len=wl.context,
+            out=self.out, k_prefix=self.pre[0], v_prefix=self.pre[1], k_recent=self.rec[0], v_recent=self.rec[1],
+            rot=self.rot, workspace=self.ws, workspace_bytes=self.ws_bytes)
+
+    def step(self, events=None, evict_events=None):
+        E = self.torch.cuda.Event
+        for t in range(self.wl.loops):
+            for l in range(self.wl.layers):
+                if events is not None:
+                    e0, e1 = E(enable_timing=True), E(enable_timing=True)
+                    e0.record()
+                    self.decode(l, t)
+                    e1.record()
+                    events.append((e0, e1))
+                else:
+                    self.decode(l, t)
 
 
 def cpu_baseline(wl, seconds: float) -> dict:
@@ -754,6 +816,9 @@ def main():
     ap.add_argument("--plan", default=None,
                     help="decode mode: per-(layer, loop range) choice of (c, G), e.g. '8:4x4,24:8x4' "
                          "(layers separated by '/'; one entry applies to every layer)")
+    ap.add_argument("--bf16-cache", action="store_true",
+                    help="decode mode: the same kernel over an uncompressed bf16 cache (recent window = whole "
+                         "context, no vector-quantized tokens), for the comparison with the packed cache")
     ap.add_argument("--lloyd", action="store_true",
                     help="time one weighted Lloyd iteration of one codebook set instead of the decode step "
                          "(default workload for this mode: deep4x32_h32_d128_b16_n8k)")
@@ -784,7 +849,14 @@ def main():
         wl = wl.with_(name=wl.name + "_cbj", codebook_per_loop_group=True)
     torch.cuda.set_device(0)
     plan = parse_plan(args.plan, wl) if args.plan else None
-    bench = MixedBench(wl, plan) if plan else Bench(wl)
+    if args.bf16_cache and plan:
+        print(json.dumps({"error": "--bf16-cache takes no --plan"}))
+        sys.exit(2)
+    if args.bf16_cache:
+        bench = Bf16Bench(wl)
+        wl = bench.wl
+    else:
+        bench = MixedBench(wl, plan) if plan else Bench(wl)
     for _ in range(args.warmup):
         bench.step()
     torch.cuda.synchronize()
@@ -816,21 +888,27 @@ def main():
     log(f"wall {wall:.2f}s for {args.steps} steps; launch avg {avg_us:.1f} us (p10 {np.percentile(launch_us, 10):.1f}, "
         f"p90 {np.percentile(launch_us, 90):.1f}); {achieved:.0f} GB/s")
     rec = {
-        "metric": METRIC, "value": value, "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "metric": BF16_METRIC if args.bf16_cache else METRIC, "value": value, "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl.name, "layers": wl.layers, "loop_steps": wl.loops, "loop_group": wl.loop_group,
                    "q_heads": wl.q_heads, "kv_heads": wl.kv_heads, "head_dim": wl.head_dim, "batch": wl.batch,
                    "context": wl.context, "prefix_tokens": wl.prefix, "recent_tokens": wl.recent,
                    "chans_per_group": wl.chans, "index_bits": wl.index_bits,
-                   "bits_per_elem": (plan_bits_per_elem(plan, wl.index_bits) if plan
+                   "bits_per_elem": (16.0 if args.bf16_cache else
+                                     plan_bits_per_elem(plan, wl.index_bits) if plan
                                      else wl.index_bits / (wl.chans * wl.loop_group)),
+                   "cache": ("bf16: recent window = context - prefix, no vector-quantized tokens; one (layer, "
+                             "loop step) K / V window pair (17.2 GB at 32K) is read by every launch of the step"
+                             if args.bf16_cache else "packed indices + bf16 prefix / recent windows"),
                    "page_tokens": wl.page_tokens,
                    "codebook_per_loop_group": bool(wl.codebook_per_loop_group),
                    "plan": args.plan,
                    "launches_per_step": wl.layers * wl.loops,
-                   "eviction_launches_per_step": sum(len(s) for s in plan) if plan else 1,
+                   "eviction_launches_per_step": 0 if args.bf16_cache else (sum(len(s) for s in plan) if plan else 1),
                    "evicted_sub_vectors_per_step": (
+                       0 if args.bf16_cache else
                        sum((n // G) * 2 * wl.batch * wl.kv_heads * (wl.head_dim // c)
                            for segs in plan for n, c, G in segs) if plan
                        else wl.layers * wl.loop_groups * 2 * wl.batch * wl.kv_heads * wl.groups)},
@@ -839,7 +917,8 @@ def main():
         "decode_launch_us": {"mean": avg_us, "p10": float(np.percentile(launch_us, 10)),
                              "p50": float(np.percentile(launch_us, 50)), "p90": float(np.percentile(launch_us, 90))},
         "algorithmic_bytes_per_launch": ab,
-        "evict_launch_us": float(np.mean([a.elapsed_time(b) * 1e3 for a, b in evict_events])),
+        "evict_launch_us": (float(np.mean([a.elapsed_time(b) * 1e3 for a, b in evict_events]))
+                            if evict_events else None),
         "step_gbps": ab["total"] * wl.layers * wl.loops / (step_ms * 1e-3) / 1e9,
     }
     if not args.no_cpu_baseline:

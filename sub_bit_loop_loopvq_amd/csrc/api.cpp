@@ -115,10 +115,13 @@ int min_splits(const loopvq_config* c, int32_t max_seq_len) {
 int plan_splits(const loopvq_config* c, int32_t batch, int32_t max_seq_len) {
   const int64_t Q = int64_t(batch) * c->num_q_heads;
   const int64_t n_vq = std::max<int64_t>(0, int64_t(max_seq_len) - c->prefix_tokens - c->recent_tokens);
+  const int64_t n_win = std::min<int64_t>(max_seq_len, int64_t(c->prefix_tokens) + c->recent_tokens);
   const int64_t tiles = (n_vq + decode_tile_tokens(c) - 1) / decode_tile_tokens(c);
+  // work in 2 KB index tiles (1 KB of K and of V indices); a bf16 window row moves 4 d bytes
+  const int64_t work = tiles + (n_win * 4 * c->head_dim + 2047) / 2048;
   const int64_t slots = (c->head_dim / c->chans_per_group) == 32 ? 256 : 512;  // resident workgroups
   int64_t S = Q >= slots ? 1 : (slots + Q - 1) / Q;
-  const int64_t max_by_work = std::max<int64_t>(1, tiles / 32);   // >= 32 tiles per split
+  const int64_t max_by_work = std::max<int64_t>(1, work / 32);   // >= 32 tiles of work per split
   S = std::min(S, max_by_work);
   S = std::max<int64_t>(S, min_splits(c, max_seq_len));
   return (int)std::max<int64_t>(1, std::min<int64_t>(S, 256));

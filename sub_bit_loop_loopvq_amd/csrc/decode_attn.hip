@@ -37,7 +37,8 @@
 //    reproducible; LDS float atomics are an order of magnitude slower on this
 //    part).  Afterwards o[g*c + i] = sum_k H[k][g] * Cv_tau[k][g*c + i] and the
 //    normaliser is sum_k H[k][0]: the same quantised weights.
-//  * bf16 windows: lane-per-token scores, then lane-per-channel value sums.
+//  * bf16 windows: a wave step reads 1 KB of K and of V rows (16 B per lane), DPP row sums
+//    give the scores, and each lane accumulates p * V for its 8 channels.
 //  * splits write (m, l, o) partials; a second kernel merges them with
 //    log-sum-exp.  One split writes the output directly.
 #include "lvq_common.h"
@@ -124,11 +125,10 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
   constexpr int G4 = NG / 4;        // lanes that share a token quad
   constexpr int TW = 256 / G4;      // tokens per wave tile (1 KB of 8-bit indices)
   constexpr int NT = WAVES * 64;
-  constexpr int CPL = D / 64;       // window channels per lane
   constexpr int LPT = kCodes * NG / NT;   // LUT entries built per thread
   constexpr int NPG = kMaxTilesPerWave / 64;
   static_assert(NG == 16 || NG == 32, "NG");
-  static_assert(CPL == 1 || CPL == 2 || CPL == 4, "D");
+  static_assert(D == 64 || D == 128, "D");
   static_assert(LPT >= 1 && NT % NG == 0, "LUT build mapping");
   using SliceT = typename std::conditional<C == 4, uint2, uint4>::type;
 
@@ -271,72 +271,106 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
     zero_hist(sm, tid);
   }
 
-  // ---- 3. bf16 window rows (prefix + recent) of this split: one token per wave at a
-  //         time, lanes over channels, four tokens' loads in flight -------------------
-  float m_w = kNegInf, l_w = 0.f, o_w[CPL];
+  // ---- 3. bf16 window rows (prefix + recent) of this split --------------------------------
+  //  A wave step covers RPI rows: lane (wr, wc) loads channels [8 wc, 8 wc + 8) of row wr of
+  //  the step (16 B of K and 16 B of V, so one step reads 1 KB of each), forms the partial
+  //  dot product, and a DPP sum over the row's LPR lanes gives every lane its row's score.
+  //  Steps are dealt to the waves round robin with four in flight per wave.  The softmax
+  //  reference m_w only moves up when a score passes it by more than 8 (log2 units), so
+  //  p <= 2^8 and rescaling is rare after the first step.
+  constexpr int LPR = D / 8;      // lanes per window row
+  constexpr int RPI = 64 / LPR;   // rows per wave step
+  float m_w = kNegInf, l_w = 0.f, o8[8];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) o_w[c] = 0.f;
+  for (int c = 0; c < 8; ++c) o8[c] = 0.f;
   {
+    const int wr = lane / LPR, wc = lane % LPR;
+    float qv[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qv[c] = sm.q[8 * wc + c];
     const int64_t pre_row0 = ((int64_t)b * p.Hkv + h) * p.P;
     const int64_t rec_row0 = ((int64_t)b * p.Hkv + h) * p.R;
-    float qc[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) qc[c] = sm.q[lane * CPL + c];
-    auto row_of = [&](const uint16_t* pre, const uint16_t* rec, int w) -> const uint16_t* {
-      return (w < n_prefix) ? pre + (pre_row0 + w) * D : rec + (rec_row0 + (w - n_prefix)) * D;
+    const int wstride = WAVES * RPI;
+    const int wfirst = w0 + wave * RPI;
+    const int n_ws = wfirst < w1 ? (w1 - wfirst + wstride - 1) / wstride : 0;
+    auto wload = [&](int i, u32x4& kk, u32x4& vv) {   // rows past the split end re-read its last row
+      int w = wfirst + i * wstride + wr;
+      w = w < w1 ? w : w1 - 1;
+      const bool pre = w < n_prefix;
+      const int64_t off = (pre ? pre_row0 + w : rec_row0 + (w - n_prefix)) * D + 8 * wc;
+      kk = ntload(reinterpret_cast<const u32x4*>((pre ? p.k_prefix : p.k_recent) + off));
+      vv = ntload(reinterpret_cast<const u32x4*>((pre ? p.v_prefix : p.v_recent) + off));
     };
-    auto load_ch = [&](const uint16_t* row, float* dst) {
-      if constexpr (CPL == 1) {
-        dst[0] = bf16_at(row + lane);
-      } else if constexpr (CPL == 2) {
-        const uint32_t v2 = *reinterpret_cast<const uint32_t*>(row + 2 * lane);
-        dst[0] = bf16_lo(v2);
-        dst[1] = bf16_hi(v2);
-      } else {
-        const uint2 v4 = *reinterpret_cast<const uint2*>(row + 4 * lane);
-        dst[0] = bf16_lo(v4.x);
-        dst[1] = bf16_hi(v4.x);
-        dst[2] = bf16_lo(v4.y);
-        dst[3] = bf16_hi(v4.y);
+    auto wstep = [&](const u32x4 kk, const u32x4 vv, int i) {
+      const bool live = wfirst + i * wstride + wr < w1;
+      const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
+      float d = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        d = fmaf(qv[2 * j], bf16_lo(kw[j]), d);
+        d = fmaf(qv[2 * j + 1], bf16_hi(kw[j]), d);
+      }
+      d += dpp<dpp_quad(1, 0, 3, 2)>(d);
+      d += dpp<dpp_quad(2, 3, 0, 1)>(d);
+      d += dpp<kDppRowHalfMirror>(d);
+      if constexpr (LPR == 16) d += dpp<kDppRowMirror>(d);
+      const float sc = live ? d : kNegInf;
+      if (__builtin_amdgcn_ballot_w64(sc > m_w + 8.f) != 0) {   // first step, or a new maximum
+        const float mn = fmaxf(m_w, wave_max_nolds(sc));
+        const float a = __builtin_amdgcn_exp2f(m_w - mn);          // 0 on the first step
+        l_w *= a;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o8[c] *= a;
+        m_w = mn;
+      }
+      const float pw = live ? __builtin_amdgcn_exp2f(sc - m_w) : 0.f;
+      l_w += pw;
+      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o8[2 * j] = fmaf(pw, bf16_lo(vw[j]), o8[2 * j]);
+        o8[2 * j + 1] = fmaf(pw, bf16_hi(vw[j]), o8[2 * j + 1]);
       }
     };
-    constexpr int WU = 4;
-    for (int wb = w0 + wave; wb < w1; wb += WAVES * WU) {
-      float kx[WU][CPL], vx[WU][CPL];
+    if (n_ws > 0) {
+      u32x4 kb[kPF], vb[kPF];
 #pragma unroll
-      for (int j = 0; j < WU; ++j) {
-        const int w = wb + j * WAVES;
-        if (w < w1) {
-          load_ch(row_of(p.k_prefix, p.k_recent, w), kx[j]);
-          load_ch(row_of(p.v_prefix, p.v_recent, w), vx[j]);
+      for (int j = 0; j < kPF; ++j) wload(j < n_ws ? j : n_ws - 1, kb[j], vb[j]);
+      const int n_full = n_ws - n_ws % kPF;
+      for (int i0 = 0; i0 < n_full; i0 += kPF) {
+#pragma unroll
+        for (int j = 0; j < kPF; ++j) {
+          __builtin_amdgcn_sched_barrier(0);
+          wstep(kb[j], vb[j], i0 + j);
+          wload(i0 + j + kPF < n_ws ? i0 + j + kPF : n_ws - 1, kb[j], vb[j]);
         }
       }
 #pragma unroll
-      for (int j = 0; j < WU; ++j) {
-        const int w = wb + j * WAVES;
-        if (w < w1) {
-          float d = 0.f;
+      for (int j = 0; j < kPF - 1; ++j)
+        if (n_full + j < n_ws) wstep(kb[j], vb[j], n_full + j);
+    }
+    // sum l and o over the wave's row groups (lanes with the same chunk wc)
+    auto row_sum = [&](float v) -> float {
+      if constexpr (LPR == 8) v += dpp<kDppRowRor8>(v);
+      const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+      uint32_t h0, h1;
+      halves(__float_as_uint(v), h0, h1);
+      return __uint_as_float(h0) + __uint_as_float(h1);
+    };
+    l_w = row_sum(l_w);
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) d = fmaf(qc[c], kx[j][c], d);
-          d = wave_sum(d);
-          const float mn = fmaxf(m_w, d);
-          const float a = __builtin_amdgcn_exp2f(m_w - mn);
-          const float pw = __builtin_amdgcn_exp2f(d - mn);
-          l_w = fmaf(l_w, a, pw);
+    for (int c = 0; c < 8; ++c) o8[c] = row_sum(o8[c]);
+    // all threads finished the rotation scratch reads (barrier after q') before these writes
+    if (lane == 0) {
+      sm.wm[wave] = m_w;
+      sm.wl[wave] = l_w;
+    }
+    if (lane < LPR) {
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) o_w[c] = fmaf(o_w[c], a, pw * vx[j][c]);
-          m_w = mn;
-        }
-      }
+      for (int c = 0; c < 8; ++c) sm.wo[wave][8 * lane + c] = o8[c];
     }
   }
-  // all threads finished the rotation scratch reads (barrier after q') before these writes
-  if (lane == 0) {
-    sm.wm[wave] = m_w;
-    sm.wl[wave] = l_w;
-  }
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) sm.wo[wave][lane * CPL + c] = o_w[c];
 
   __syncthreads();   // LUT, histogram zeroing and window partials complete
 

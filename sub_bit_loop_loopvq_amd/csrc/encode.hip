@@ -53,29 +53,8 @@ __device__ __forceinline__ uint32_t neg2_bf16x2(uint32_t w) {
   return (w ^ 0x80008000u) + __builtin_bit_cast(uint32_t, inc);
 }
 
-// (value of half 0, value of half 1) of a wave register, in every lane
-__device__ __forceinline__ void halves(uint32_t v, uint32_t& h0, uint32_t& h1) {
-  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  h0 = r[0];
-  h1 = r[1];
-}
-
-// maximum over the wave without LDS: quad, half-row and row mirrors, then the row pairs and
-// the wave halves
-__device__ __forceinline__ float wave_max_nolds(float v) {
-  v = fmaxf(v, dpp<0xb1>(v));    // quad_perm [1, 0, 3, 2]
-  v = fmaxf(v, dpp<0x4e>(v));    // quad_perm [2, 3, 0, 1]
-  v = fmaxf(v, dpp<0x141>(v));   // row_half_mirror
-  v = fmaxf(v, dpp<0x140>(v));   // row_mirror
-  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
-  uint32_t h0, h1;
-  halves(__float_as_uint(v), h0, h1);
-  return fmaxf(__uint_as_float(h0), __uint_as_float(h1));
-}
-
-// value of a packed key with its index bits cleared
-__device__ __forceinline__ float key_value(float k) { return __uint_as_float(__float_as_uint(k) & 0xffffff00u); }
+// value of a packed key with its 7 index bits cleared
+__device__ __forceinline__ float key_value(float k) { return __uint_as_float(__float_as_uint(k) & 0xffffff80u); }
 
 // last word of a raw (unstructured, byte-addressed) buffer resource on CDNA
 constexpr int kRawBufferWord3 = 0x00020000;

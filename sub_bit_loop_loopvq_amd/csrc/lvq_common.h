@@ -133,6 +133,8 @@ __device__ __forceinline__ float bf16_at(const uint16_t* p) { return __uint_as_f
 // DPP controls (GCN/CDNA encoding)
 constexpr int dpp_quad(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
 constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowRor8 = 0x128;   // lane i of a 16-lane row reads lane i ^ 8
 
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.  Block L runs
 // on XCD L % 8; give XCD x the contiguous range of logical blocks that starts where the
@@ -157,6 +159,27 @@ __device__ __forceinline__ float codeword_norm(const uint16_t* row, int E) {
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// (value of half 0, value of half 1) of a wave register, in every lane
+__device__ __forceinline__ void halves(uint32_t v, uint32_t& h0, uint32_t& h1) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  h0 = r[0];
+  h1 = r[1];
+}
+
+// maximum over the wave without LDS: quad, half-row and row mirrors, then the row pairs and
+// the wave halves
+__device__ __forceinline__ float wave_max_nolds(float v) {
+  v = fmaxf(v, dpp<dpp_quad(1, 0, 3, 2)>(v));
+  v = fmaxf(v, dpp<dpp_quad(2, 3, 0, 1)>(v));
+  v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppRowMirror>(v));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  uint32_t h0, h1;
+  halves(__float_as_uint(v), h0, h1);
+  return fmaxf(__uint_as_float(h0), __uint_as_float(h1));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
