@@ -333,16 +333,19 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
       }
     };
     if (n_ws > 0) {
+      // only steps that exist are loaded (the streaming loads bypass the caches, so a
+      // repeated row would be read from HBM again)
       u32x4 kb[kPF], vb[kPF];
 #pragma unroll
-      for (int j = 0; j < kPF; ++j) wload(j < n_ws ? j : n_ws - 1, kb[j], vb[j]);
+      for (int j = 0; j < kPF; ++j)
+        if (j < n_ws) wload(j, kb[j], vb[j]);
       const int n_full = n_ws - n_ws % kPF;
       for (int i0 = 0; i0 < n_full; i0 += kPF) {
 #pragma unroll
         for (int j = 0; j < kPF; ++j) {
           __builtin_amdgcn_sched_barrier(0);
           wstep(kb[j], vb[j], i0 + j);
-          wload(i0 + j + kPF < n_ws ? i0 + j + kPF : n_ws - 1, kb[j], vb[j]);
+          if (i0 + j + kPF < n_ws) wload(i0 + j + kPF, kb[j], vb[j]);
         }
       }
 #pragma unroll
