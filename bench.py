@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "VQ decode-attn queries/s + effective HBM GB/s (% peak), 32K ctx, 0.5 bit/elem"
 BF16_METRIC = "bf16-cache decode-attn queries/s + effective HBM GB/s (% peak), same kernel, 32K ctx"
 HBM_PEAK_GBPS = 8000.0
+MIN_ROTATED_CACHE_BYTES = 4 * 256 * 2**20   # 4x the Infinity Cache
 DEFAULT_WORKLOAD = "stack24x4_h16_d128_b64_n32k"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stack32k_traffic.md")
 DECODE_SRC = os.path.join(ROOT, "sub_bit_loop_loopvq_amd", "csrc", "decode_attn.hip")
@@ -141,16 +142,27 @@ class Bench:
         self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
         self.evict_pos = torch.full((B,), n_vq - 1, dtype=torch.int32, device=dev)
         self.evict_slot = torch.zeros((B,), dtype=torch.int32, device=dev)
+        # A cache smaller than 4x the 256 MB Infinity Cache would be served from it when launches
+        # repeat: decode launches then rotate over copies of the pool and windows, so every
+        # launch reads its bytes from HBM (the eviction keeps writing copy 0).
+        cache_bytes = self.lay.pool_bytes + 2 * (self.pre[0].numel() + self.rec[0].numel()) * 2
+        self.replicas = max(1, min(16, -(-MIN_ROTATED_CACHE_BYTES // cache_bytes)))
+        self.reps = [(self.pool, self.pre, self.rec)]
+        for _ in range(self.replicas - 1):
+            self.reps.append((self.pool.clone(), self.pre.clone(), self.rec.clone()))
+        self.rep_i = 0
         self.setup_s = time.time() - t0
         log(f"setup done in {self.setup_s:.1f}s; re-ranked sub-vectors during build: {int(self.rerank.item())}")
 
     def decode(self, l, t):
         wl = self.wl
+        pool, pre, rec = self.reps[self.rep_i]
+        self.rep_i = (self.rep_i + 1) % self.replicas
         self.lvq.loopvq_decode_attn(
             self.cfg, layer=l, loop=t, batch=wl.batch, q=self.q[l, t], seq_lens=self.lens, max_seq_len=wl.context,
-            out=self.out, block_table=self.bt, pool=self.pool, max_pages_per_seq=self.pages_per_seq,
-            num_pages=self.num_pages, cb_k_prep=self.prep[0], cb_v_prep=self.prep[1], k_prefix=self.pre[0, l, t],
-            v_prefix=self.pre[1, l, t], k_recent=self.rec[0, l, t], v_recent=self.rec[1, l, t], rot=self.rot,
+            out=self.out, block_table=self.bt, pool=pool, max_pages_per_seq=self.pages_per_seq,
+            num_pages=self.num_pages, cb_k_prep=self.prep[0], cb_v_prep=self.prep[1], k_prefix=pre[0, l, t],
+            v_prefix=pre[1, l, t], k_recent=rec[0, l, t], v_recent=rec[1, l, t], rot=self.rot,
             workspace=self.ws, workspace_bytes=self.ws_bytes)
 
     def evict(self):
@@ -906,6 +918,9 @@ def main():
                    "codebook_per_loop_group": bool(wl.codebook_per_loop_group),
                    "plan": args.plan,
                    "launches_per_step": wl.layers * wl.loops,
+                   "cache_replicas": (1 if args.bf16_cache else
+                                      min(b.replicas for row in bench.segs for _, b in row) if plan
+                                      else bench.replicas),
                    "eviction_launches_per_step": 0 if args.bf16_cache else (sum(len(s) for s in plan) if plan else 1),
                    "evicted_sub_vectors_per_step": (
                        0 if args.bf16_cache else

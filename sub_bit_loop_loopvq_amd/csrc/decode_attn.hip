@@ -158,6 +158,28 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
   const int w0 = (int)(((int64_t)n_win * s) / p.S);
   const int w1 = (int)(((int64_t)n_win * (s + 1)) / p.S);
   const int n_tiles = (n_vq + TW - 1) / TW;
+
+  // bf16 window rows of this split, in wave steps of RPI rows: lane (wr, wc) holds channels
+  // [8 wc, 8 wc + 8) of row wr of a step.  The wave's first step is requested here, ahead of
+  // the page-id chain and the prologue, which its latency then overlaps.
+  constexpr int LPR = D / 8;      // lanes per window row
+  constexpr int RPI = 64 / LPR;   // rows per wave step
+  const int wr = lane / LPR, wc = lane % LPR;
+  const int64_t pre_row0 = ((int64_t)b * p.Hkv + h) * p.P;
+  const int64_t rec_row0 = ((int64_t)b * p.Hkv + h) * p.R;
+  const int wstride = WAVES * RPI;
+  const int wfirst = w0 + wave * RPI;
+  const int n_ws = wfirst < w1 ? (w1 - wfirst + wstride - 1) / wstride : 0;
+  auto wload = [&](int i, u32x4& kk, u32x4& vv) {   // rows past the split end re-read its last row
+    int w = wfirst + i * wstride + wr;
+    w = w < w1 ? w : w1 - 1;
+    const bool pre = w < n_prefix;
+    const int64_t off = (pre ? pre_row0 + w : rec_row0 + (w - n_prefix)) * D + 8 * wc;
+    kk = ntload(reinterpret_cast<const u32x4*>((pre ? p.k_prefix : p.k_recent) + off));
+    vv = ntload(reinterpret_cast<const u32x4*>((pre ? p.v_prefix : p.v_recent) + off));
+  };
+  u32x4 wk0, wv0;
+  if (n_ws > 0) wload(0, wk0, wv0);
   const int t0 = (int)(((int64_t)n_tiles * s) / p.S);
   const int t1 = (int)(((int64_t)n_tiles * (s + 1)) / p.S);
   const bool has_vq = t1 > t0;
@@ -278,29 +300,13 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
   //  Steps are dealt to the waves round robin with four in flight per wave.  The softmax
   //  reference m_w only moves up when a score passes it by more than 8 (log2 units), so
   //  p <= 2^8 and rescaling is rare after the first step.
-  constexpr int LPR = D / 8;      // lanes per window row
-  constexpr int RPI = 64 / LPR;   // rows per wave step
   float m_w = kNegInf, l_w = 0.f, o8[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) o8[c] = 0.f;
   {
-    const int wr = lane / LPR, wc = lane % LPR;
     float qv[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) qv[c] = sm.q[8 * wc + c];
-    const int64_t pre_row0 = ((int64_t)b * p.Hkv + h) * p.P;
-    const int64_t rec_row0 = ((int64_t)b * p.Hkv + h) * p.R;
-    const int wstride = WAVES * RPI;
-    const int wfirst = w0 + wave * RPI;
-    const int n_ws = wfirst < w1 ? (w1 - wfirst + wstride - 1) / wstride : 0;
-    auto wload = [&](int i, u32x4& kk, u32x4& vv) {   // rows past the split end re-read its last row
-      int w = wfirst + i * wstride + wr;
-      w = w < w1 ? w : w1 - 1;
-      const bool pre = w < n_prefix;
-      const int64_t off = (pre ? pre_row0 + w : rec_row0 + (w - n_prefix)) * D + 8 * wc;
-      kk = ntload(reinterpret_cast<const u32x4*>((pre ? p.k_prefix : p.k_recent) + off));
-      vv = ntload(reinterpret_cast<const u32x4*>((pre ? p.v_prefix : p.v_recent) + off));
-    };
     auto wstep = [&](const u32x4 kk, const u32x4 vv, int i) {
       const bool live = wfirst + i * wstride + wr < w1;
       const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
@@ -336,8 +342,10 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
       // only steps that exist are loaded (the streaming loads bypass the caches, so a
       // repeated row would be read from HBM again)
       u32x4 kb[kPF], vb[kPF];
+      kb[0] = wk0;
+      vb[0] = wv0;
 #pragma unroll
-      for (int j = 0; j < kPF; ++j)
+      for (int j = 1; j < kPF; ++j)
         if (j < n_ws) wload(j, kb[j], vb[j]);
       const int n_full = n_ws - n_ws % kPF;
       for (int i0 = 0; i0 < n_full; i0 += kPF) {
