@@ -831,6 +831,8 @@ def main():
     ap.add_argument("--bf16-cache", action="store_true",
                     help="decode mode: the same kernel over an uncompressed bf16 cache (recent window = whole "
                          "context, no vector-quantized tokens), for the comparison with the packed cache")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode mode: also capture one step in a HIP graph and time its replays (launch overhead)")
     ap.add_argument("--lloyd", action="store_true",
                     help="time one weighted Lloyd iteration of one codebook set instead of the decode step "
                          "(default workload for this mode: deep4x32_h32_d128_b16_n8k)")
@@ -885,6 +887,29 @@ def main():
     wall = time.perf_counter() - t0
     step_ms = ev0.elapsed_time(ev1) / args.steps
     launch_us = np.array([a.elapsed_time(b) * 1e3 for a, b in events])
+    graph = None
+    if args.graph:
+        # the same step captured once and replayed: the difference is the host launch overhead
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            bench.step()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            bench.step()
+        g.replay()
+        torch.cuda.synchronize()
+        gv0, gv1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gv0.record()
+        for _ in range(args.steps):
+            g.replay()
+        gv1.record()
+        torch.cuda.synchronize()
+        g_ms = gv0.elapsed_time(gv1) / args.steps
+        graph = {"ms_per_step": g_ms, "queries_per_s": wl.layers * wl.loops * wl.queries_per_launch / (g_ms * 1e-3),
+                 "eager_minus_graph_ms": step_ms - g_ms}
+        log(f"graph replay: {g_ms:.3f} ms per step (eager {step_ms:.3f} ms)")
     if plan:   # bytes of a launch averaged over the segments' launches
         ab_l = [algorithmic_bytes(wl.with_(chans=c, loop_group=G)) for segs in plan for n, c, G in segs
                 for _ in range(n)]
@@ -936,6 +961,8 @@ def main():
                             if evict_events else None),
         "step_gbps": ab["total"] * wl.layers * wl.loops / (step_ms * 1e-3) / 1e9,
     }
+    if graph is not None:
+        rec["graph"] = graph
     if not args.no_cpu_baseline:
         # with a plan: the oracle on the workload of layer 0's first segment
         base = wl.with_(chans=plan[0][0][1], loop_group=plan[0][0][2]) if plan else wl
