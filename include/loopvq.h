@@ -280,7 +280,8 @@ typedef struct loopvq_decode_args {
   int32_t max_pages_per_seq;
   int32_t max_seq_len;          /* upper bound of seq_lens[] (sizes the split plan) */
   int32_t num_splits;           /* 0 = automatic, else 1..256 */
-  int64_t num_pages;            /* pages per (layer, loop group, kv-head) */
+  int64_t num_pages;            /* pages per (layer, loop group, kv-head); with VQ rows,
+                                   num_pages * page_bytes < 2^31 (else LOOPVQ_ERR_UNSUPPORTED) */
   const uint16_t* q;            /* device bf16 [B][Hq][d] */
   const int32_t* seq_lens;      /* device [B], each in [1, max_seq_len] */
   const int32_t* block_table;   /* device [B][max_pages_per_seq] */

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -491,6 +492,8 @@ loopvq_status loopvq_decode_attn(const loopvq_config* cfg, const loopvq_decode_a
   if (S < min_splits(cfg, a->max_seq_len) || S > 256)
     return fail(LOOPVQ_ERR_INVALID_ARG, "num_splits %d: a context of %d tokens needs between %d and 256 splits", S,
                 a->max_seq_len, min_splits(cfg, a->max_seq_len));
+  if (can_vq && int64_t(a->num_pages) * z.page_bytes > INT32_MAX)
+    return fail(LOOPVQ_ERR_UNSUPPORTED, "num_pages * page_bytes (one kv-head's page region) must stay below 2 GiB");
   const int64_t Q = int64_t(a->batch) * cfg->num_q_heads;
   const size_t need = S > 1 ? size_t(S) * Q * (cfg->head_dim + 4) * sizeof(float) : 0;
   if (workspace_bytes < need || (need && !workspace))

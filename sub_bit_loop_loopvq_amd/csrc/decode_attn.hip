@@ -187,7 +187,12 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
   // ---- 0. issue the first global loads: page ids, the first index tiles, the key
   //         codebook slice and q, so their latency overlaps the prologue -------------
   const int Qd = lane / G4, u = lane % G4;
-  const uint8_t* pool_h = has_vq ? p.pool_lj + (int64_t)h * p.head_stride + lane * 16 : nullptr;
+  // index tiles come through buffer loads over the kv-head's page region (below 2 GiB, checked
+  // by the host): the tile offset is uniform (a scalar register) and each lane adds 16 B
+  const uint8_t* pool_h = has_vq ? p.pool_lj + (int64_t)h * p.head_stride : p.pool_lj;
+  const __amdgpu_buffer_rsrc_t pool_rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)pool_h, (short)0, 0x7fffffff, kRawBufferWord3);
+  const int lane16 = lane * 16;
   const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
   const int pt_mask = (1 << p.pt_shift) - 1;
   const int my_first = t0 + wave;
@@ -205,7 +210,7 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
     }
     pg[c] = v;
   }
-  auto tile_ptr = [&](int i) -> const uint8_t* {   // i: wave-uniform tile ordinal
+  auto tile_off = [&](int i) -> int {   // i: wave-uniform tile ordinal; byte offset in the region
     const int c = i >> 6, l = i & 63;
     int page = __builtin_amdgcn_readlane(pg[0], l);
 #pragma unroll
@@ -214,16 +219,16 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
       page = c == cc ? pc : page;
     }
     const int u0 = (my_first + i * WAVES) * TW;
-    return pool_h + (int64_t)page * p.page_bytes + (int64_t)(u0 & pt_mask) * NG;
+    return page * (int)p.page_bytes + (u0 & pt_mask) * NG;
   };
   constexpr int kPF = 4;
   u32x4 bk[kPF], bv[kPF];
   auto load_first = [&]() {
 #pragma unroll
     for (int j = 0; j < kPF; ++j) {
-      const uint8_t* pa = tile_ptr(j < n_my ? j : n_my - 1);
-      bk[j] = ntload(reinterpret_cast<const u32x4*>(pa));
-      bv[j] = ntload(reinterpret_cast<const u32x4*>(pa + p.kind_bytes));
+      const int to = tile_off(j < n_my ? j : n_my - 1);
+      bk[j] = __builtin_amdgcn_raw_buffer_load_b128(pool_rs, lane16, to, kBufNontemporal);
+      bv[j] = __builtin_amdgcn_raw_buffer_load_b128(pool_rs, lane16, to + (int)p.kind_bytes, kBufNontemporal);
     }
   };
   if (n_my > 0) load_first();
@@ -444,24 +449,24 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
       to_fixed(pp, fh, fl);
       uint32_t ph[4], pl[4];
       if constexpr (NG == 16) {
-        ph[0] = __builtin_amdgcn_update_dpp(0, fh, dpp_quad(0, 0, 0, 0), 0xf, 0xf, false);
-        ph[1] = __builtin_amdgcn_update_dpp(0, fh, dpp_quad(1, 1, 1, 1), 0xf, 0xf, false);
-        ph[2] = __builtin_amdgcn_update_dpp(0, fh, dpp_quad(2, 2, 2, 2), 0xf, 0xf, false);
-        ph[3] = __builtin_amdgcn_update_dpp(0, fh, dpp_quad(3, 3, 3, 3), 0xf, 0xf, false);
-        pl[0] = __builtin_amdgcn_update_dpp(0, fl, dpp_quad(0, 0, 0, 0), 0xf, 0xf, false);
-        pl[1] = __builtin_amdgcn_update_dpp(0, fl, dpp_quad(1, 1, 1, 1), 0xf, 0xf, false);
-        pl[2] = __builtin_amdgcn_update_dpp(0, fl, dpp_quad(2, 2, 2, 2), 0xf, 0xf, false);
-        pl[3] = __builtin_amdgcn_update_dpp(0, fl, dpp_quad(3, 3, 3, 3), 0xf, 0xf, false);
+        ph[0] = __builtin_amdgcn_mov_dpp(fh, dpp_quad(0, 0, 0, 0), 0xf, 0xf, false);
+        ph[1] = __builtin_amdgcn_mov_dpp(fh, dpp_quad(1, 1, 1, 1), 0xf, 0xf, false);
+        ph[2] = __builtin_amdgcn_mov_dpp(fh, dpp_quad(2, 2, 2, 2), 0xf, 0xf, false);
+        ph[3] = __builtin_amdgcn_mov_dpp(fh, dpp_quad(3, 3, 3, 3), 0xf, 0xf, false);
+        pl[0] = __builtin_amdgcn_mov_dpp(fl, dpp_quad(0, 0, 0, 0), 0xf, 0xf, false);
+        pl[1] = __builtin_amdgcn_mov_dpp(fl, dpp_quad(1, 1, 1, 1), 0xf, 0xf, false);
+        pl[2] = __builtin_amdgcn_mov_dpp(fl, dpp_quad(2, 2, 2, 2), 0xf, 0xf, false);
+        pl[3] = __builtin_amdgcn_mov_dpp(fl, dpp_quad(3, 3, 3, 3), 0xf, 0xf, false);
       } else {
         // token i of the quad lives in lanes 2i, 2i+1 of the 8-lane group
-        const uint32_t ah = __builtin_amdgcn_update_dpp(0, fh, dpp_quad(0, 0, 0, 0), 0xf, 0xf, false);
-        const uint32_t bh = __builtin_amdgcn_update_dpp(0, fh, dpp_quad(2, 2, 2, 2), 0xf, 0xf, false);
-        const uint32_t al = __builtin_amdgcn_update_dpp(0, fl, dpp_quad(0, 0, 0, 0), 0xf, 0xf, false);
-        const uint32_t bl = __builtin_amdgcn_update_dpp(0, fl, dpp_quad(2, 2, 2, 2), 0xf, 0xf, false);
-        const uint32_t amh = __builtin_amdgcn_update_dpp(0, ah, kDppRowHalfMirror, 0xf, 0xf, false);
-        const uint32_t bmh = __builtin_amdgcn_update_dpp(0, bh, kDppRowHalfMirror, 0xf, 0xf, false);
-        const uint32_t aml = __builtin_amdgcn_update_dpp(0, al, kDppRowHalfMirror, 0xf, 0xf, false);
-        const uint32_t bml = __builtin_amdgcn_update_dpp(0, bl, kDppRowHalfMirror, 0xf, 0xf, false);
+        const uint32_t ah = __builtin_amdgcn_mov_dpp(fh, dpp_quad(0, 0, 0, 0), 0xf, 0xf, false);
+        const uint32_t bh = __builtin_amdgcn_mov_dpp(fh, dpp_quad(2, 2, 2, 2), 0xf, 0xf, false);
+        const uint32_t al = __builtin_amdgcn_mov_dpp(fl, dpp_quad(0, 0, 0, 0), 0xf, 0xf, false);
+        const uint32_t bl = __builtin_amdgcn_mov_dpp(fl, dpp_quad(2, 2, 2, 2), 0xf, 0xf, false);
+        const uint32_t amh = __builtin_amdgcn_mov_dpp(ah, kDppRowHalfMirror, 0xf, 0xf, false);
+        const uint32_t bmh = __builtin_amdgcn_mov_dpp(bh, kDppRowHalfMirror, 0xf, 0xf, false);
+        const uint32_t aml = __builtin_amdgcn_mov_dpp(al, kDppRowHalfMirror, 0xf, 0xf, false);
+        const uint32_t bml = __builtin_amdgcn_mov_dpp(bl, kDppRowHalfMirror, 0xf, 0xf, false);
         ph[0] = hi_half ? amh : ah;
         ph[1] = hi_half ? bmh : bh;
         ph[2] = hi_half ? ah : amh;
@@ -517,9 +522,9 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
             __builtin_amdgcn_sched_barrier(0);
             process(bk[j], bv[j], i0 + j);
             const int inext = (i0 + j + kPF < n_my) ? (i0 + j + kPF) : (n_my - 1);
-            const uint8_t* pa = tile_ptr(inext);
-            bk[j] = ntload(reinterpret_cast<const u32x4*>(pa));
-            bv[j] = ntload(reinterpret_cast<const u32x4*>(pa + p.kind_bytes));
+            const int to = tile_off(inext);
+            bk[j] = __builtin_amdgcn_raw_buffer_load_b128(pool_rs, lane16, to, kBufNontemporal);
+            bv[j] = __builtin_amdgcn_raw_buffer_load_b128(pool_rs, lane16, to + (int)p.kind_bytes, kBufNontemporal);
           }
         }
 #pragma unroll

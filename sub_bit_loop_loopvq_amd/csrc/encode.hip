@@ -56,8 +56,6 @@ __device__ __forceinline__ uint32_t neg2_bf16x2(uint32_t w) {
 // value of a packed key with its 7 index bits cleared
 __device__ __forceinline__ float key_value(float k) { return __uint_as_float(__float_as_uint(k) & 0xffffff80u); }
 
-// last word of a raw (unstructured, byte-addressed) buffer resource on CDNA
-constexpr int kRawBufferWord3 = 0x00020000;
 
 // channel groups per kv-head the kernels take (d / c <= 32)
 constexpr int kMaxGroups = 32;

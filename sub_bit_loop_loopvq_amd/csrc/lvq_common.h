@@ -132,6 +132,10 @@ __device__ __forceinline__ float bf16_at(const uint16_t* p) { return __uint_as_f
 
 // DPP controls (GCN/CDNA encoding)
 constexpr int dpp_quad(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
+// last word of a raw (unstructured, byte-addressed) buffer resource on CDNA
+constexpr int kRawBufferWord3 = 0x00020000;
+// cache-policy operand of a buffer load: nontemporal (streamed once)
+constexpr int kBufNontemporal = 2;
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
 constexpr int kDppRowRor8 = 0x128;   // lane i of a 16-lane row reads lane i ^ 8
@@ -158,7 +162,7 @@ __device__ __forceinline__ float codeword_norm(const uint16_t* row, int E) {
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
 // (value of half 0, value of half 1) of a wave register, in every lane
