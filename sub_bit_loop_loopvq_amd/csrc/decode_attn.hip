@@ -144,6 +144,20 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
   const int hq = qi - b * p.Hq;
   const int h = hq / (p.Hq / p.Hkv);
 
+  // With one split, a wave's tiles are wave, wave + WAVES, ... whatever the sequence length is,
+  // so their page ids are requested together with the length instead of after it (entries are
+  // clamped to the block-table row; lanes past the sequence's tiles are cleared below).
+  const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
+  const bool pg_early = p.S == 1 && p.max_pages > 0;
+  int pg_raw[NPG];
+  if (pg_early) {
+#pragma unroll
+    for (int c = 0; c < NPG; ++c) {
+      const int e = ((wave + (64 * c + lane) * WAVES) * TW) >> p.pt_shift;
+      pg_raw[c] = bt[e < p.max_pages ? e : p.max_pages - 1];
+    }
+  }
+
   int N = p.seq_lens[b];
   N = N < 0 ? 0 : (N > p.max_seq_len ? p.max_seq_len : N);
   const int n_prefix = N < p.P ? N : p.P;
@@ -170,13 +184,19 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
   const int wstride = WAVES * RPI;
   const int wfirst = w0 + wave * RPI;
   const int n_ws = wfirst < w1 ? (w1 - wfirst + wstride - 1) / wstride : 0;
+  // (the window bases as values: a per-lane choice between two argument fields would otherwise
+  // be made by loading the chosen field from the argument block, one dependent load per call)
+  const uint16_t* const kpre = p.k_prefix;
+  const uint16_t* const vpre = p.v_prefix;
+  const uint16_t* const krec = p.k_recent;
+  const uint16_t* const vrec = p.v_recent;
   auto wload = [&](int i, u32x4& kk, u32x4& vv) {   // rows past the split end re-read its last row
     int w = wfirst + i * wstride + wr;
     w = w < w1 ? w : w1 - 1;
     const bool pre = w < n_prefix;
     const int64_t off = (pre ? pre_row0 + w : rec_row0 + (w - n_prefix)) * D + 8 * wc;
-    kk = ntload(reinterpret_cast<const u32x4*>((pre ? p.k_prefix : p.k_recent) + off));
-    vv = ntload(reinterpret_cast<const u32x4*>((pre ? p.v_prefix : p.v_recent) + off));
+    kk = ntload(reinterpret_cast<const u32x4*>((pre ? kpre : krec) + off));
+    vv = ntload(reinterpret_cast<const u32x4*>((pre ? vpre : vrec) + off));
   };
   u32x4 wk0, wv0;
   if (n_ws > 0) wload(0, wk0, wv0);
@@ -193,22 +213,31 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
   const __amdgpu_buffer_rsrc_t pool_rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)pool_h, (short)0, 0x7fffffff, kRawBufferWord3);
   const int lane16 = lane * 16;
-  const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
   const int pt_mask = (1 << p.pt_shift) - 1;
   const int my_first = t0 + wave;
   const int n_my = (has_vq && my_first < t1) ? (t1 - my_first + WAVES - 1) / WAVES : 0;
 
   // page ids of this wave's tiles: lane l of pg[c] holds the page of tile 64*c + l
+  // (two separate paths, so that the early ids are waited for without the loads issued after
+  // them)
   int pg[NPG];
+  if (pg_early) {
 #pragma unroll
-  for (int c = 0; c < NPG; ++c) {
-    const int i = 64 * c + lane;
-    int v = 0;
-    if (i < n_my) {
-      v = bt[((my_first + i * WAVES) * TW) >> p.pt_shift];
-      v = (v < 0 || v >= p.num_pages) ? 0 : v;
+    for (int c = 0; c < NPG; ++c) {
+      const int v = pg_raw[c];
+      pg[c] = (64 * c + lane < n_my && v >= 0 && v < p.num_pages) ? v : 0;
     }
-    pg[c] = v;
+  } else {
+#pragma unroll
+    for (int c = 0; c < NPG; ++c) {
+      const int i = 64 * c + lane;
+      int v = 0;
+      if (i < n_my) {
+        v = bt[((my_first + i * WAVES) * TW) >> p.pt_shift];
+        v = (v < 0 || v >= p.num_pages) ? 0 : v;
+      }
+      pg[c] = v;
+    }
   }
   auto tile_off = [&](int i) -> int {   // i: wave-uniform tile ordinal; byte offset in the region
     const int c = i >> 6, l = i & 63;
