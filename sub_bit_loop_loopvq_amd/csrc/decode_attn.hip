@@ -72,6 +72,7 @@ struct DecodeSmem {
   float wm[WAVES], wl[WAVES];                   // window partial max / sum per wave
   float vm[WAVES];                              // VQ max per wave
   int vover[WAVES];
+  float lpart[16];                              // normaliser partials of the value contraction
 };
 
 // Byte offset (from LDS address 0) of histogram entry (k, g).
@@ -519,7 +520,7 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
 
     // reference maximum: the first tile of every wave (already in flight)
     float m_loc = kNegInf;
-    if (n_my > 0) m_loc = wave_max(score(bk[0], my_first == n_tiles - 1, 0));
+    if (n_my > 0) m_loc = wave_max_nolds(score(bk[0], my_first == n_tiles - 1, 0));
     if (lane == 0) sm.vm[wave] = m_loc;
     __syncthreads();
     m_ref = sm.vm[0];
@@ -560,7 +561,7 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
         for (int j = 0; j < kPF - 1; ++j)
           if (n_full + j < n_my) process(bk[j], bv[j], n_full + j);
       }
-      smax = wave_max(smax);
+      smax = wave_max_nolds(smax);
       const bool wover = __any(over);
       if (lane == 0) {
         sm.vm[wave] = smax;
@@ -588,7 +589,7 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
   constexpr int CP = D / 2;
   constexpr int PARTS = NT / CP;
   constexpr int KPT = kCodes / PARTS;
-  static_assert(NT % CP == 0 && kCodes % PARTS == 0, "contraction mapping");
+  static_assert(NT % CP == 0 && kCodes % PARTS == 0 && PARTS <= 16, "contraction mapping");
   float o_vq = 0.f, l_vq = 0.f;
   if (has_vq) {
     const int cp = tid % CP, part = tid / CP, g = (2 * cp) / C;
@@ -596,34 +597,31 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
     uint32_t cv[KPT];
 #pragma unroll
     for (int m = 0; m < KPT; ++m) cv[m] = *reinterpret_cast<const uint32_t*>(sv + (part + m * PARTS) * D);
-    float a0 = 0.f, a1 = 0.f;
+    float a0 = 0.f, a1 = 0.f, lsum = 0.f;
 #pragma unroll
     for (int m = 0; m < KPT; ++m) {
       const unsigned long long hv = *reinterpret_cast<const unsigned long long*>(lds + hist_off<NG>(part + m * PARTS, g));
       const float hk = fmaf((float)(uint32_t)(hv >> 32), 4294967296.f, (float)(uint32_t)hv);
       a0 = fmaf(hk, bf16_lo(cv[m]), a0);
       a1 = fmaf(hk, bf16_hi(cv[m]), a1);
+      lsum += hk;
     }
     sm.red[part * D + 2 * cp] = a0;
     sm.red[part * D + 2 * cp + 1] = a1;
-  }
-  __syncthreads();
-  if (has_vq && tid < 64) {
-    // normaliser: the quantised weights of group 0 sum to l * 2^30
-    unsigned long long t = 0;
-#pragma unroll
-    for (int k = tid; k < kCodes; k += 64) t += *reinterpret_cast<const unsigned long long*>(lds + hist_off<NG>(k, 0));
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) t += __shfl_xor(t, m, 64);
-    if (tid == 0) sm.vm[0] = fmaf((float)(uint32_t)(t >> 32), 4294967296.f, (float)(uint32_t)t) * (1.f / kFix);
+    // normaliser: the quantised weights of group 0 (the same values the products used) sum to
+    // l * 2^30; the thread of channel pair 0 of each part holds that part's share
+    if (cp == 0) sm.lpart[part] = lsum;
   }
   __syncthreads();
   if (tid < D) {
     if (has_vq) {
 #pragma unroll
-      for (int pp = 0; pp < PARTS; ++pp) o_vq += sm.red[pp * D + tid];
+      for (int pp = 0; pp < PARTS; ++pp) {
+        o_vq += sm.red[pp * D + tid];
+        l_vq += sm.lpart[pp];
+      }
       o_vq *= 1.f / kFix;
-      l_vq = sm.vm[0];
+      l_vq *= 1.f / kFix;
     }
     const bool vq_live = has_vq && l_vq > 0.f;
     float M = vq_live ? m_ref : kNegInf;
