@@ -44,6 +44,22 @@ def test_whole_context_window(splits):
     _say(f"  rel/max={H.check_attention(o, o_ref, lse, lse_ref)}")
 
 
+@pytest.mark.parametrize("scale", [64.0, 4096.0])
+def test_whole_context_window_peaked(scale):
+    """Queries scaled by 2^6 and 2^12 (exact in bf16): scores span hundreds of log2 units, so the
+    softmax reference of the window steps moves many times (each time a score passes it by 8)."""
+    from synth import gen
+    _say(f"whole-context bf16 window, queries x{scale}")
+    wl = ALL_BF16
+    case = H.Case(wl, 0, 3, [1500, 700, 999])
+    case.q = gen.to_bf16_bits(gen.bf16_to_f64(case.q) * scale)
+    empty = np.zeros((0, wl.groups), np.int64)
+    o_ref, lse_ref = case.oracle_decode(lambda k, b, h: empty)
+    case.gpu_setup()
+    o, lse = case.gpu_decode(num_splits=0)
+    _say(f"  rel/max={H.check_attention(o, o_ref, lse, lse_ref)}")
+
+
 @pytest.mark.parametrize("splits", [0, 1, 3])
 def test_wide_window_beside_vq_rows(splits):
     _say(f"600-row recent window + vector-quantized rows, splits={splits}")
