@@ -186,16 +186,4 @@ __device__ __forceinline__ float wave_max_nolds(float v) {
   return fmaxf(__uint_as_float(h0), __uint_as_float(h1));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
-}
-
 }  // namespace lvq
