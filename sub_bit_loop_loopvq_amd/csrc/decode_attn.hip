@@ -531,35 +531,55 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
     for (int pass = 0; pass < 2; ++pass) {
       float smax = kNegInf;
       bool over = false;
-      auto process = [&](const u32x4 xk, const u32x4 xv, int i) {
+      // Software pipeline over the wave's tiles: the key lookups of tile i are issued in the
+      // same region as the value atomics of tile i-1, so each wave keeps LDS reads in flight
+      // while its atomics issue; a slot is refilled once its value indices are consumed.
+      auto score_of = [&](const u32x4 xk, int i) -> float {
         const bool masked = (my_first + i * WAVES) == n_tiles - 1;   // only the globally last tile is partial
-        const float sc = score(xk, masked, i);
+        return score(xk, masked, i);
+      };
+      auto finish = [&](const u32x4 xv, float sc) {
         smax = fmaxf(smax, sc);
         const float e = sc - m_ref;
         over |= e > kThr;
         accum_v(xv, __builtin_amdgcn_exp2f(fminf(e, kThr)));
       };
+      auto refill = [&](int slot_tile, u32x4& xk, u32x4& xv) {
+        const int inext = slot_tile < n_my ? slot_tile : n_my - 1;
+        const int to = tile_off(inext);
+        xk = __builtin_amdgcn_raw_buffer_load_b128(pool_rs, lane16, to, kBufNontemporal);
+        xv = __builtin_amdgcn_raw_buffer_load_b128(pool_rs, lane16, to + (int)p.kind_bytes, kBufNontemporal);
+      };
       if (n_my > 0) {
         if (pass > 0) load_first();
-        // steady state: branch-free, every slot refilled (clamped to the last tile; refills
-        // past the end re-read a valid tile and are never consumed)
-        const int n_full = n_my - n_my % kPF;
-        for (int i0 = 0; i0 < n_full; i0 += kPF) {
+        float sc_prev = score_of(bk[0], 0);
+        // steady state over tiles 1 .. n_my-1 in groups of kPF: tile i = i0 + j + 1 sits in slot
+        // (j + 1) % kPF, its predecessor in slot j; refills past the end re-read the last tile
+        // and are never consumed
+        const int n_rest = n_my - 1;
+        const int n_full = n_rest - n_rest % kPF;
+        int i0 = 0;
+        for (; i0 < n_full; i0 += kPF) {
 #pragma unroll
           for (int j = 0; j < kPF; ++j) {
-            // keep each slot's work in program order: hoisting a later slot's index
-            // arithmetic above this point would stall on that slot's in-flight load
             __builtin_amdgcn_sched_barrier(0);
-            process(bk[j], bv[j], i0 + j);
-            const int inext = (i0 + j + kPF < n_my) ? (i0 + j + kPF) : (n_my - 1);
-            const int to = tile_off(inext);
-            bk[j] = __builtin_amdgcn_raw_buffer_load_b128(pool_rs, lane16, to, kBufNontemporal);
-            bv[j] = __builtin_amdgcn_raw_buffer_load_b128(pool_rs, lane16, to + (int)p.kind_bytes, kBufNontemporal);
+            const float sc = score_of(bk[(j + 1) % kPF], i0 + j + 1);
+            finish(bv[j], sc_prev);
+            refill(i0 + j + kPF, bk[j], bv[j]);
+            sc_prev = sc;
           }
         }
 #pragma unroll
-        for (int j = 0; j < kPF - 1; ++j)
-          if (n_full + j < n_my) process(bk[j], bv[j], n_full + j);
+        for (int j = 0; j < kPF; ++j) {
+          const int i = i0 + j + 1;
+          if (i < n_my) {
+            const float sc = score_of(bk[(j + 1) % kPF], i);
+            finish(bv[j], sc_prev);
+            sc_prev = sc;
+          } else if (i == n_my) {
+            finish(bv[j], sc_prev);
+          }
+        }
       }
       smax = wave_max_nolds(smax);
       const bool wover = __any(over);
@@ -688,11 +708,6 @@ hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
 }
 
 }  // namespace
-
-// Largest number of vector-quantized tokens one split may cover: keeps every 64-bit histogram
-// sum below 2^64 (one token adds at most 2^47) and a wave's tiles within its page-id vector
-// (256 tiles per wave x 8 waves).
-int decode_max_split_tokens(int ng) { return ng == 32 ? 65536 : 65536; }
 
 hipError_t launch_decode(const DecodeParams& p, int ng, int c, hipStream_t stream) {
   if (ng == 32 && c == 4) return launch_variant<32, 4>(p, stream);
