@@ -83,6 +83,20 @@ def test_small_ragged_chain(splits):
     _chain(case, decode_splits=splits)
 
 
+@pytest.mark.parametrize("c,lens", [(4, [2147, 2819, 4451, 4771]), (8, [2179, 3011, 4227, 4867])])
+def test_tile_count_sweep_chain(c, lens):
+    """One split, with lengths chosen so that the waves' tile counts run through 4..10: the tile loop
+    keeps four tiles in flight, and these counts reach every remainder of its steady state, each
+    sequence with a ragged last tile (c=4: 32-token tiles over 16 waves, 65/86/137/147 tiles;
+    c=8: 64-token tiles over 8 waves, 33/46/65/75 tiles)."""
+    if c == 4:
+        wl = SMALL.with_(batch=4, q_heads=2, kv_heads=1, context=4800)
+    else:
+        wl = W.QUARTER_16K.with_(layers=1, batch=4, q_heads=2, kv_heads=1, context=4900)
+    _say(f"tile-count sweep c={c} lens={lens}")
+    _chain(H.Case(wl, 0, 1, lens, seed=11), decode_splits=(1, 0))
+
+
 def test_gqa_chain():
     wl = SMALL.with_(batch=2, q_heads=8, kv_heads=2, context=600)
     _say("gqa chain")
