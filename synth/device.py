@@ -50,7 +50,7 @@ class DeviceGen:
     def __init__(self, wl: Workload, device="cuda"):
         import torch
         self.wl = wl
-        self.table = torch.from_numpy(np.ascontiguousarray(gen.normal_table())).to(device)
+        self.table = torch.from_numpy(np.array(gen.normal_table(), copy=True)).to(device)
         self.scales_np = gen.scales(wl)
         self.scales = torch.from_numpy(np.ascontiguousarray(self.scales_np)).to(device)
         self.signs = (torch.from_numpy(gen.rotation_signs(wl)).to(device) if wl.rotate_keys else None)
