@@ -842,7 +842,7 @@ def main():
                          "(default workload for this mode: deep4x32_h32_d128_b16_n8k)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 5)
