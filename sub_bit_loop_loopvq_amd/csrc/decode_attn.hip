@@ -519,8 +519,11 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
     };
 
     // reference maximum: the first tile of every wave (already in flight)
-    float m_loc = kNegInf;
-    if (n_my > 0) m_loc = wave_max_nolds(score(bk[0], my_first == n_tiles - 1, 0));
+    float m_loc = kNegInf, sc_first = kNegInf;   // the first tile's scores also start pass 0
+    if (n_my > 0) {
+      sc_first = score(bk[0], my_first == n_tiles - 1, 0);
+      m_loc = wave_max_nolds(sc_first);
+    }
     if (lane == 0) sm.vm[wave] = m_loc;
     __syncthreads();
     m_ref = sm.vm[0];
@@ -552,7 +555,7 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
       };
       if (n_my > 0) {
         if (pass > 0) load_first();
-        float sc_prev = score_of(bk[0], 0);
+        float sc_prev = pass == 0 ? sc_first : score_of(bk[0], 0);
         // steady state over tiles 1 .. n_my-1 in groups of kPF: tile i = i0 + j + 1 sits in slot
         // (j + 1) % kPF, its predecessor in slot j; refills past the end re-read the last tile
         // and are never consumed
