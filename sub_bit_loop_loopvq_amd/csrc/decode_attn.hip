@@ -70,6 +70,7 @@ struct DecodeSmem {
   float red[2 * WAVES * 64];                    // raw q, then contraction partials
   float wo[WAVES][D];                           // window partial o per wave
   float wm[WAVES], wl[WAVES];                   // window partial max / sum per wave
+  float vm0[WAVES];                             // first-tile VQ max per wave (the reference)
   float vm[WAVES];                              // VQ max per wave
   int vover[WAVES];
   float lpart[16];                              // normaliser partials of the value contraction
@@ -524,12 +525,11 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
       sc_first = score(bk[0], my_first == n_tiles - 1, 0);
       m_loc = wave_max_nolds(sc_first);
     }
-    if (lane == 0) sm.vm[wave] = m_loc;
+    if (lane == 0) sm.vm0[wave] = m_loc;   // slots of their own: no barrier before the pass reuses vm
     __syncthreads();
-    m_ref = sm.vm[0];
+    m_ref = sm.vm0[0];
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) m_ref = fmaxf(m_ref, sm.vm[w]);
-    __syncthreads();
+    for (int w = 1; w < WAVES; ++w) m_ref = fmaxf(m_ref, sm.vm0[w]);
 
     for (int pass = 0; pass < 2; ++pass) {
       float smax = kNegInf;
