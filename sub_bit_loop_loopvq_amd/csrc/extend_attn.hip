@@ -396,6 +396,12 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
     }
     for (int k = 0; k < n_tiles; ++k) {
       __syncthreads();                // tile k is staged; every wave is done with tile k - 1
+      ks = ks2[k & 1];
+      vt = vt2[k & 1];
+      const Tile tl = tile_of(k);
+      consume(tl.count, tl.seg == 3 ? tl.start : -1);
+      // tile k + 1 is staged after the products of tile k are issued, so the staging work runs
+      // while they drain (its buffer last served tile k - 1, which the barrier above closed)
       if (k + 1 < n_tiles) {
         ks = ks2[(k + 1) & 1];
         vt = vt2[(k + 1) & 1];
@@ -405,10 +411,6 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
           if (k + 3 < n_tiles) fetch_idx(k + 3, ik_n, iv_n, ok_n);
         }
       }
-      ks = ks2[k & 1];
-      vt = vt2[k & 1];
-      const Tile tl = tile_of(k);
-      consume(tl.count, tl.seg == 3 ? tl.start : -1);
     }
   } else {
     for (int k = 0; k < n_tiles; ++k) {
