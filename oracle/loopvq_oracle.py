@@ -227,7 +227,11 @@ def unpack_sequence(pages: np.ndarray, n: int, NG: int, PT: int, b: int):
 
 def pool_offset(l: int, j: int, h: int, page: int, J: int, Hkv: int, num_pages: int,
                 page_bytes: int) -> int:
-    """Byte offset of a page in the pool [L][J][Hkv][num_pages][page_bytes]."""
+    """Byte offset of a page in the pool [L][J][Hkv][num_pages][page_bytes].
+
+    [AIR] "Raisons" says only that the indices are stored packed; this pool order (layer,
+    loop group, kv-head, page, row-major) is the reading that the library shares.
+    """
     return (((l * J + j) * Hkv + h) * num_pages + page) * page_bytes
 
 
@@ -254,6 +258,11 @@ def attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float,
     qq = np.asarray(q, dtype=np.float64)
     if rot is not None:
         qq = np.asarray(rot, dtype=np.float64).T @ qq
+    if keys.shape[0] == 0:
+        # an empty context (N = 0): the softmax sum is empty, so lse = ln 0 = -inf, and the
+        # output is the empty sum of weighted values, 0 (reading: the pages never decode
+        # with nothing cached; this is the limit a caller can rely on)
+        return np.zeros(values.shape[1], dtype=np.float64), -np.inf
     s = scale * (keys @ qq)
     m = s.max()
     p = np.exp(s - m)
@@ -263,7 +272,9 @@ def attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float,
 
 
 def split_context(N: int, P: int, R: int):
-    """(n_prefix, n_vq, n_recent) for a sequence of N cached tokens ([AIR] "Utilisation")."""
+    """(n_prefix, n_vq, n_recent) for a sequence of N >= 0 cached tokens ([AIR] "Utilisation")."""
+    if N < 0:
+        raise ValueError("a sequence holds N >= 0 tokens")
     n_prefix = min(P, N)
     n_vq = max(0, N - P - R)
     return n_prefix, n_vq, N - n_prefix - n_vq
@@ -307,14 +318,25 @@ def extend_attention(q_rows, k_prefix, v_prefix, idx_k, idx_v, cb_k, cb_v, k_rec
 # Codebook learning: weighted Lloyd iterations
 # ---------------------------------------------------------------------------
 def round_to_bf16(v: np.ndarray) -> np.ndarray:
-    """fp64 -> nearest bf16 value (8 significant bits, ties to even), returned as fp64.
+    """fp64 -> nearest bf16 value (round half to even), returned as fp64.
 
-    Written out from the definition: v = m * 2**e with 0.5 <= |m| < 1, so the nearest
-    bf16 is round_half_even(m * 2**8) * 2**(e - 8).  (Normal range only.)
+    Written out from the format: bf16 keeps 8 significant bits and the fp32 exponent
+    range.  With v = m * 2**e, 0.5 <= |m| < 1, a normal bf16 near v is spaced 2**(e - 8)
+    apart; below the smallest normal 2**-126 (e < -125) the spacing stays 2**-133
+    (subnormals).  So the result is round_half_even(v / q) * q with q = 2**(max(e, -125) - 8).
+    A magnitude that rounds above the largest finite bf16, (2 - 2**-7) * 2**127, becomes
+    an infinity of the same sign (the tie at the overflow threshold rounds up, to the
+    even significand), as IEEE round-to-nearest-even prescribes.
     """
     v = np.asarray(v, dtype=np.float64)
-    m, e = np.frexp(v)
-    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
+    _, e = np.frexp(v)
+    qe = np.maximum(e, -125) - 8
+    r = np.ldexp(np.round(np.ldexp(v, -qe)), qe)
+    big = np.abs(r) > BF16_MAX
+    return np.where(big, np.copysign(np.inf, v), r)
+
+
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
 
 
 def lloyd_step(x: np.ndarray, w: np.ndarray, C: np.ndarray, to_bf16: bool = True):

@@ -164,10 +164,12 @@ class Case:
         self.d_q = dev_u16(self.q)
         self.d_win = [dev_u16(a) for a in (self.kp, self.vp, self.kr, self.vr)]
         self.d_rot = dev_f32(self.rot) if self.rot is not None else None
-        # the pool holds only this (layer, loop group): hand the library a base shifted back by its offset
+        # the pool holds only this (layer, loop group): hand the library a base shifted back by the
+        # slice's offset in the whole pool (the oracle's statement of the pool order)
         self.slice_bytes = wl.kv_heads * lay.pool_head_stride_bytes
         self.d_pool = torch.zeros(self.slice_bytes, dtype=torch.uint8, device=DEV)
-        self.pool_shift = (self.l * wl.loop_groups + self.j) * self.slice_bytes
+        self.pool_shift = O.pool_offset(self.l, self.j, 0, 0, wl.loop_groups, wl.kv_heads, self.paging.num_pages,
+                                        lay.page_bytes)
 
     def pool_base(self) -> int:
         return self.d_pool.data_ptr() - self.pool_shift
@@ -314,12 +316,14 @@ class FullCase:
         self.d_rot = dev_f32(self.rot) if self.rot is not None else None
         slice_bytes = wl.kv_heads * lay.pool_head_stride_bytes
         self.d_pool = torch.zeros(slice_bytes, dtype=torch.uint8, device=DEV)
-        self.pool_shift = (self.l * wl.loop_groups + self.j) * slice_bytes
         pb = lay.page_bytes
+        at = lambda h, page: O.pool_offset(self.l, self.j, h, page, wl.loop_groups, wl.kv_heads,  # noqa: E731
+                                           self.paging.num_pages, pb)
+        self.pool_shift = at(0, 0)
         for b, h in self.pairs:
             pages = O.pack_sequence(self.idx[0, b, h], self.idx[1, b, h], wl.page_tokens, wl.index_bits)
             for p in range(pages.shape[0]):
-                off = h * lay.pool_head_stride_bytes + int(self.paging.table[b, p]) * pb
+                off = at(h, int(self.paging.table[b, p])) - self.pool_shift
                 self.d_pool[off:off + pb] = torch.from_numpy(pages[p]).to(DEV)
         torch.cuda.synchronize()
 

@@ -475,6 +475,71 @@ def test_round_to_bf16_matches_the_bit_level_rounding():
     assert O.round_to_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
 
 
+def _all_finite_bf16():
+    """Every finite non-negative bf16 value, in increasing order, from its bit patterns (an fp32
+    whose low 16 bits are zero is exactly one bf16)."""
+    bits = np.arange(0, 0x7F80, dtype=np.uint32) << np.uint32(16)
+    return bits, bits.view(np.float32).astype(np.float64)
+
+
+def test_round_to_bf16_over_the_whole_format():
+    """Brute force over all 32,640 finite non-negative bf16 values (subnormals included): each
+    is kept, each gap's midpoint goes to the neighbour with the even pattern, and values just
+    inside a gap go to the nearer end; past the largest finite value the result overflows to
+    infinity exactly from the rounding threshold on.  The sign is symmetric."""
+    bits, vals = _all_finite_bf16()
+    a, b = vals[:-1], vals[1:]
+    mid = (a + b) / 2.0                              # exact in fp64
+    eps = (b - a) * 2.0 ** -20
+    assert np.array_equal(O.round_to_bf16(vals), vals)
+    assert np.array_equal(O.round_to_bf16(-vals), -vals)
+    assert np.array_equal(O.round_to_bf16(mid - eps), a)
+    assert np.array_equal(O.round_to_bf16(mid + eps), b)
+    even_lo = ((bits[:-1] >> np.uint32(16)) & np.uint32(1)) == 0
+    assert np.array_equal(O.round_to_bf16(mid), np.where(even_lo, a, b))
+    assert np.array_equal(O.round_to_bf16(-mid), -np.where(even_lo, a, b))
+    top = vals[-1]                                   # largest finite bf16, pattern 0x7F7F
+    assert bits[-1] == 0x7F7F << 16 and top == O.BF16_MAX
+    step = 2.0 ** (127 - 7)
+    thr = top + step / 2                             # halfway to 2^128: rounds up, to even
+    assert O.round_to_bf16(np.array([thr - step * 2.0 ** -20]))[0] == top
+    assert O.round_to_bf16(np.array([thr, 1e39, 1e300]))[0] == np.inf
+    assert np.all(np.isinf(O.round_to_bf16(np.array([thr, 1e39, 1e300]))))
+    assert O.round_to_bf16(np.array([-thr]))[0] == -np.inf
+    # far below the smallest subnormal 2^-133: zero; half of it ties to zero (even)
+    assert np.array_equal(O.round_to_bf16(np.array([1e-300, 2.0 ** -134, 2.0 ** -134 * 1.0000001])),
+                          np.array([0.0, 0.0, 2.0 ** -133]))
+
+
+def test_pool_offset_is_the_row_major_pool_index():
+    """pool_offset against numpy's own row-major indexing of [L][J][Hkv][num_pages][page_bytes]."""
+    L, J, Hkv, num_pages, page_bytes = 3, 2, 5, 7, 16
+    pool = np.arange(L * J * Hkv * num_pages * page_bytes).reshape(L, J, Hkv, num_pages, page_bytes)
+    for l, j, h, pg in itertools.product(range(L), range(J), range(Hkv), range(num_pages)):
+        assert O.pool_offset(l, j, h, pg, J, Hkv, num_pages, page_bytes) == pool[l, j, h, pg, 0]
+    # a transposed pair of indices (kv-head and loop group swapped) is caught
+    assert O.pool_offset(0, 1, 0, 0, J, Hkv, num_pages, page_bytes) != O.pool_offset(0, 0, 1, 0, J, Hkv, num_pages,
+                                                                                       page_bytes)
+
+
+def test_empty_context_is_zero_output_and_minus_infinite_lse():
+    """N = 0: an empty softmax (sum of no terms); N < 0 is not a context."""
+    d = 8
+    z = np.zeros((0, d))
+    cb = [np.zeros((4, 4))] * (d // 4)
+    o, lse = O.decode_query(np.ones(d), z, z, np.zeros((0, d // 4), int), np.zeros((0, d // 4), int), cb, cb,
+                            z, z, 0, 4, 1.0)
+    assert np.array_equal(o, np.zeros(d)) and lse == -np.inf
+    assert O.split_context(0, 8, 64) == (0, 0, 0)
+    with pytest.raises(ValueError):
+        O.split_context(-1, 8, 64)
+    # one token more: its value row, lse = its score (the N = 1 closed form still holds)
+    k1, v1 = np.ones((1, d)), np.arange(d, dtype=float)[None]
+    o, lse = O.decode_query(np.ones(d), k1, v1, np.zeros((0, d // 4), int), np.zeros((0, d // 4), int), cb, cb,
+                            z, z, 0, 4, 0.5)
+    assert np.array_equal(o, v1[0]) and lse == pytest.approx(0.5 * d, rel=1e-15)
+
+
 def test_lloyd_hand_example():
     x = np.array([[0.0], [1.0], [10.0], [11.0]])
     w = np.array([1.0, 3.0, 1.0, 1.0])
