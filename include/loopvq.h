@@ -108,6 +108,12 @@ typedef struct loopvq_layout {
 } loopvq_layout;
 
 /* Validate a configuration: the rules above (ranges, divisibility, page size).
+ * Source: one codebook index covers c channels of G consecutive loop steps
+ * (airadar.tv summary, opening paragraph; arXiv 2611.05304 English abstract:
+ * the channels of several loop steps are coded jointly), so T must split into
+ * whole loop groups and d into whole channel groups; P and R are the bf16
+ * prefix / recent token counts of the serving launch line (airadar.tv summary,
+ * section "Utilisation": 8 and 64).
  * Returns LOOPVQ_OK or LOOPVQ_ERR_INVALID_ARG; never touches the GPU. */
 loopvq_status loopvq_config_check(const loopvq_config* cfg);
 
@@ -116,11 +122,23 @@ loopvq_status loopvq_config_check(const loopvq_config* cfg);
 double loopvq_bits_per_elem(const loopvq_config* cfg);
 
 /* Fill *out with the sizes above for `batch` sequences and a pool of
- * `num_pages` pages per (layer, loop group, kv-head).  Host only. */
+ * `num_pages` pages per (layer, loop group, kv-head).  Source: the serving
+ * path stores the codebook indices packed (airadar.tv summary, section
+ * "Raisons"); the page and micro-tile order above is this library's own
+ * reading of that storage, and the bf16 window sizes follow the prefix /
+ * recent counts (section "Utilisation").  Host only; returns
+ * LOOPVQ_ERR_INVALID_ARG for an invalid config, a NULL out, batch < 1 or
+ * num_pages < 1. */
 loopvq_status loopvq_layout_query(const loopvq_config* cfg, int32_t batch, int64_t num_pages,
                                   loopvq_layout* out);
 
 /* Derive the decode-side codebook copies from canonical codebooks.
+ * Source: the model ships a codebook folder (airadar.tv summary, section
+ * "Utilisation") with one codebook per (layer, kv-head, channel group) whose
+ * rows span G loop steps (opening paragraph); a decode launch of loop step t
+ * only needs slice tau = t mod G of every row, so this copy makes that slice
+ * one contiguous block.  Errors: INVALID_ARG (bad config, NULL cb or
+ * cb_prep), MISALIGNED, HIP (failed launch).
  *   cb        device, bf16 canonical [L][Jcb][Hkv][NG][K][c*G] (one kind)
  *   cb_prep   device, bf16 prepared  [L][Jcb][Hkv][G][K][d]   (written)
  *   cb_norms  device, fp32 [L][Jcb][Hkv][NG][K] squared norms (written; may be NULL)
@@ -139,6 +157,15 @@ loopvq_status loopvq_codebook_prepare_groups(const loopvq_config* cfg, const uin
 /* Encode: nearest codeword (plain squared Euclidean distance, lowest index on
  * ties) of every sub-vector of n_tokens token rows, for every kv-head and
  * channel group of one (layer, loop group, kind), packed into the pool.
+ * Source: a sub-vector groups the channels of G consecutive loop steps and
+ * shares one codebook index (airadar.tv summary, opening paragraph; arXiv
+ * 2611.05304 English abstract); the indices are stored packed (airadar.tv
+ * summary, section "Raisons").  The pages name no distance or tie rule: the
+ * squared Euclidean distance and the lowest index are this library's reading.
+ * Errors: INVALID_ARG (config, layer / loop group / kind out of range,
+ * n_tokens < 0, a NULL pointer the call needs, batch / pages < 1 with a pool),
+ * MISALIGNED, UNSUPPORTED (b != 8 or an unbuilt (c, G, d)), HIP (failed
+ * launch); n_tokens == 0 returns OK with no launch.
  * Sub-vector (row r, head h, group g) element tau*c + i is
  *   src[tau*stride_loop + r*stride_token + h*stride_head + g*c + i],  tau < G.
  * Distances are screened on bf16 matrix cores in fp32; whenever the two best
@@ -260,7 +287,12 @@ loopvq_status loopvq_lloyd_step(const loopvq_config* cfg, const loopvq_lloyd_arg
 loopvq_status loopvq_lloyd_update(const loopvq_config* cfg, const loopvq_lloyd_args* args, void* stream);
 
 /* Decode attention for one (layer l, loop step t) over all B sequences and Hq
- * query heads: for query (b, hq) with kv-head h = hq / (Hq/Hkv) and N =
+ * query heads.  Source: the serving path decodes with fused kernels over the
+ * packed indices (airadar.tv summary, section "Raisons"), the first 8 and last
+ * 64 tokens stay bf16 (section "Utilisation"), and each loop step reads its
+ * own cache (arXiv 2611.05304 English abstract), so a launch reads loop slice
+ * t mod G of the codebooks and index group t / G.  For query (b, hq) with
+ * kv-head h = hq / (Hq/Hkv) and N =
  * seq_lens[b] cached tokens (the token being decoded included), the keys and
  * values are [prefix rows | vector-quantized rows | recent rows] with
  * n_prefix = min(P, N), n_vq = max(0, N - P - R), n_recent = N - n_prefix - n_vq;
@@ -277,13 +309,17 @@ typedef struct loopvq_decode_args {
   int32_t layer;                /* l in [0, L) */
   int32_t loop;                 /* t in [0, T) */
   int32_t batch;                /* B > 0 */
-  int32_t max_pages_per_seq;
+  int32_t max_pages_per_seq;    /* with VQ rows, max_pages_per_seq * PT >= max_seq_len - P - R
+                                   (else LOOPVQ_ERR_INVALID_ARG) */
   int32_t max_seq_len;          /* upper bound of seq_lens[] (sizes the split plan) */
-  int32_t num_splits;           /* 0 = automatic, else 1..256 */
+  int32_t num_splits;           /* 0 = automatic, else 1..256 (at least the number a context of
+                                   max_seq_len needs: one split holds at most 65,536 VQ rows) */
   int64_t num_pages;            /* pages per (layer, loop group, kv-head); with VQ rows,
                                    num_pages * page_bytes < 2^31 (else LOOPVQ_ERR_UNSUPPORTED) */
   const uint16_t* q;            /* device bf16 [B][Hq][d] */
-  const int32_t* seq_lens;      /* device [B], each in [1, max_seq_len] */
+  const int32_t* seq_lens;      /* device [B], each in [0, max_seq_len].  0 is an empty context:
+                                   out row 0, lse -inf.  A length outside [0, max_seq_len] (which
+                                   the host cannot see) yields a NaN out row and lse. */
   const int32_t* block_table;   /* device [B][max_pages_per_seq] */
   const uint8_t* pool;          /* device index pool */
   const uint16_t* cb_k_prep;    /* device prepared key codebooks */

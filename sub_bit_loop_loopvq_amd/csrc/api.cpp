@@ -492,6 +492,12 @@ loopvq_status loopvq_decode_attn(const loopvq_config* cfg, const loopvq_decode_a
   if (S < min_splits(cfg, a->max_seq_len) || S > 256)
     return fail(LOOPVQ_ERR_INVALID_ARG, "num_splits %d: a context of %d tokens needs between %d and 256 splits", S,
                 a->max_seq_len, min_splits(cfg, a->max_seq_len));
+  if (can_vq && int64_t(a->max_seq_len) - cfg->prefix_tokens - cfg->recent_tokens >
+                    int64_t(a->max_pages_per_seq) * cfg->page_tokens)
+    return fail(LOOPVQ_ERR_INVALID_ARG,
+                "max_pages_per_seq (%d) pages of %d tokens cannot hold the %lld vector-quantized tokens of "
+                "max_seq_len %d", a->max_pages_per_seq, cfg->page_tokens,
+                (long long)(int64_t(a->max_seq_len) - cfg->prefix_tokens - cfg->recent_tokens), a->max_seq_len);
   if (can_vq && int64_t(a->num_pages) * z.page_bytes > INT32_MAX)
     return fail(LOOPVQ_ERR_UNSUPPORTED, "num_pages * page_bytes (one kv-head's page region) must stay below 2 GiB");
   const int64_t Q = int64_t(a->batch) * cfg->num_q_heads;

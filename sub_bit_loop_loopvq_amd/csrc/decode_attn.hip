@@ -9,8 +9,9 @@
 // loop-step-(t mod G) slice of that codeword.
 //
 // How (MI355X):
-//  * one workgroup = one query x one token split; 8 waves; one workgroup per CU
-//    (128 KB of LDS).
+//  * one workgroup = one query x one token split.  At NG = 32 (c = 4, d = 128): 16 waves
+//    and about 148 KB of LDS, one workgroup per CU; at NG = 16: 8 waves and about 72 KB,
+//    two workgroups per CU.
 //  * prologue: q' = scale*log2(e) * R^T q; the q.codeword lookup table
 //    LUT[k][g] = q'_g . slice_tau(C_k[g]) is built in LDS (K x NG fp32).
 //  * LDS layout, [0, 64K): one 256-byte row per codeword k holding LUT[k][g] at
@@ -160,8 +161,12 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
     }
   }
 
+  // N = 0 is an empty context (output 0, lse = -inf).  A length outside [0, max_seq_len] is a
+  // caller error the host cannot see: the query does no work and its output row and lse are
+  // written as NaN, so that it cannot pass for a result.
   int N = p.seq_lens[b];
-  N = N < 0 ? 0 : (N > p.max_seq_len ? p.max_seq_len : N);
+  const bool bad_len = N < 0 || N > p.max_seq_len;
+  N = bad_len ? 0 : N;
   const int n_prefix = N < p.P ? N : p.P;
   int n_vq = N - p.P - p.R;
   n_vq = n_vq < 0 ? 0 : n_vq;
@@ -667,8 +672,9 @@ __global__ void __launch_bounds__(WAVES * 64) decode_kernel(DecodeParams p) {
       }
     }
     if (p.S == 1) {
-      p.out[(int64_t)qi * D + tid] = ot / lt;
-      if (p.lse && tid == 0) p.lse[qi] = M * 0.6931471805599453f + logf(lt);
+      const float o_fin = bad_len ? __builtin_nanf("") : (lt > 0.f ? ot / lt : 0.f);
+      p.out[(int64_t)qi * D + tid] = o_fin;
+      if (p.lse && tid == 0) p.lse[qi] = bad_len ? __builtin_nanf("") : M * 0.6931471805599453f + logf(lt);
     } else {
       float* wsp = p.ws + ((int64_t)s * Q_total + qi) * (D + 4);
       wsp[4 + tid] = ot;
@@ -695,8 +701,12 @@ __global__ void __launch_bounds__(D) combine_kernel(DecodeParams p) {
       ot = fmaf(wsp[4 + tid], a, ot);
     }
   }
-  p.out[(int64_t)qi * D + tid] = ot / lt;
-  if (p.lse && tid == 0) p.lse[qi] = M * 0.6931471805599453f + logf(lt);
+  // the same contract as the single-split write: an empty context gives 0 and lse = -inf, a
+  // length outside [0, max_seq_len] gives NaN
+  const int n_seq = p.seq_lens[qi / p.Hq];
+  const bool bad_len = n_seq < 0 || n_seq > p.max_seq_len;
+  p.out[(int64_t)qi * D + tid] = bad_len ? __builtin_nanf("") : (lt > 0.f ? ot / lt : 0.f);
+  if (p.lse && tid == 0) p.lse[qi] = bad_len ? __builtin_nanf("") : M * 0.6931471805599453f + logf(lt);
 }
 
 template <int NG, int C>

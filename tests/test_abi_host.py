@@ -147,7 +147,56 @@ def test_decode_auto_split_workspace_is_checked():
     assert need > 0
     with pytest.raises(lvq.LoopVQError) as e:
         lvq.loopvq_decode_attn(cfg, **_decode_kw(wl, batch=1, max_seq_len=60000, workspace_bytes=need - 1,
-                                                 workspace=FAKE))
+                                                 workspace=FAKE, max_pages_per_seq=1000))
+    assert e.value.status == lvq.LOOPVQ_ERR_WORKSPACE
+
+
+def test_decode_rejects_a_block_table_shorter_than_the_context():
+    """max_seq_len - P - R vector-quantized rows need that many page slots per sequence."""
+    wl = W.STACK_32K
+    cfg = lvq.make_config(wl)
+    need = -(-(wl.context - wl.prefix - wl.recent) // wl.page_tokens)   # 511 pages of 64 tokens
+    with pytest.raises(lvq.LoopVQError) as e:
+        lvq.loopvq_decode_attn(cfg, **_decode_kw(wl, max_pages_per_seq=need - 1))
+    assert e.value.status == lvq.LOOPVQ_ERR_INVALID_ARG
+    assert "max_pages_per_seq" in lvq.loopvq_last_error()
+    # exactly enough pages passes every check up to the workspace, the last one before a launch
+    # (one sequence: the plan splits it, so the empty workspace is refused)
+    with pytest.raises(lvq.LoopVQError) as e:
+        lvq.loopvq_decode_attn(cfg, **_decode_kw(wl, batch=1, max_pages_per_seq=need))
+    assert e.value.status == lvq.LOOPVQ_ERR_WORKSPACE
+
+
+def test_decode_rejects_too_few_splits_for_the_histogram_bound():
+    """One split holds at most 65,536 vector-quantized rows (its 64-bit value histogram and the page
+    ids a wave keeps); an explicit split count below that is refused before any launch."""
+    wl = W.TINY.with_(context=2 * 65536 + 200)
+    cfg = lvq.make_config(wl)
+    kw = _decode_kw(wl, batch=1, max_seq_len=wl.context, max_pages_per_seq=4096, workspace=FAKE,
+                    workspace_bytes=1 << 30)
+    for S in (1, 2):
+        with pytest.raises(lvq.LoopVQError) as e:
+            lvq.loopvq_decode_attn(cfg, **dict(kw, num_splits=S))
+        assert e.value.status == lvq.LOOPVQ_ERR_INVALID_ARG
+        assert "splits" in lvq.loopvq_last_error()
+    # three splits are enough: the call then stops at the workspace, the last check before a launch
+    with pytest.raises(lvq.LoopVQError) as e:
+        lvq.loopvq_decode_attn(cfg, **dict(kw, num_splits=3, workspace_bytes=16))
+    assert e.value.status == lvq.LOOPVQ_ERR_WORKSPACE
+
+
+def test_decode_rejects_a_page_region_of_2_gib():
+    """Index tiles are read with 32-bit buffer offsets over one kv-head's page region, so
+    num_pages * page_bytes must stay below 2 GiB."""
+    wl = W.STACK_32K
+    cfg = lvq.make_config(wl)
+    page_bytes = lvq.loopvq_layout_query(cfg, 1, 1).page_bytes
+    too_many = (2 ** 31 - 1) // page_bytes + 1      # the first count whose region reaches 2^31 bytes
+    with pytest.raises(lvq.LoopVQError) as e:
+        lvq.loopvq_decode_attn(cfg, **_decode_kw(wl, num_pages=too_many))
+    assert e.value.status == lvq.LOOPVQ_ERR_UNSUPPORTED
+    with pytest.raises(lvq.LoopVQError) as e:   # one page fewer passes, up to the workspace check
+        lvq.loopvq_decode_attn(cfg, **_decode_kw(wl, batch=1, num_pages=too_many - 1))
     assert e.value.status == lvq.LOOPVQ_ERR_WORKSPACE
 
 
