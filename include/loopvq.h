@@ -342,6 +342,21 @@ loopvq_status loopvq_decode_attn_workspace(const loopvq_config* cfg, int32_t bat
 loopvq_status loopvq_decode_attn(const loopvq_config* cfg, const loopvq_decode_args* args,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* loopvq_decode_attn without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops and harnesses that forbid
+ * hipMalloc).  Same arguments, kernels and results as loopvq_decode_attn; the split
+ * partials go to a static device array of LOOPVQ_DECODE_STATIC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends (its address is looked up
+ * on the first call on each device).  Nothing is allocated or freed.  A split plan that
+ * needs more than the array (S * B * Hq * (d + 4) * 4 bytes with S > 1; S = 1 needs none)
+ * returns LOOPVQ_ERR_WORKSPACE before any HIP call.  Every call on one GPU shares that
+ * GPU's array, so calls that may overlap on one GPU (different streams, or a graph replay
+ * beside another call) race; calls ordered on one stream do not.  The array needs no
+ * clearing: every partial a merge reads is written by the same call. */
+#define LOOPVQ_DECODE_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+loopvq_status loopvq_decode_attn_noalloc(const loopvq_config* cfg, const loopvq_decode_args* args,
+                                         void* stream);
+
 /* Extend (chunked prefill): M new tokens of every sequence, whose keys and values are
  * still bf16, attend over the cached context plus the chunk itself.  The serving
  * path has a prefill backend of its own (airadar.tv summary, section

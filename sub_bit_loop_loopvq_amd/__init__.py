@@ -81,7 +81,7 @@ EXPORTS = ("loopvq_config_check", "loopvq_bits_per_elem", "loopvq_layout_query",
            "loopvq_codebook_prepare_groups",
            "loopvq_encode", "loopvq_evict", "loopvq_lloyd_workspace", "loopvq_lloyd_step",
            "loopvq_lloyd_update",
-           "loopvq_decode_attn_workspace", "loopvq_decode_attn",
+           "loopvq_decode_attn_workspace", "loopvq_decode_attn", "loopvq_decode_attn_noalloc",
            "loopvq_extend_attn", "loopvq_status_string", "loopvq_last_error")
 
 _lib = None
@@ -117,6 +117,8 @@ def lib() -> ctypes.CDLL:
         L.loopvq_decode_attn_workspace.restype = _I32
         L.loopvq_decode_attn.argtypes = [cfgp, ctypes.POINTER(loopvq_decode_args), _P, ctypes.c_size_t, _P]
         L.loopvq_decode_attn.restype = _I32
+        L.loopvq_decode_attn_noalloc.argtypes = [cfgp, ctypes.POINTER(loopvq_decode_args), _P]
+        L.loopvq_decode_attn_noalloc.restype = _I32
         L.loopvq_extend_attn.argtypes = [cfgp, ctypes.POINTER(loopvq_extend_args), _P]
         L.loopvq_extend_attn.restype = _I32
         L.loopvq_status_string.argtypes, L.loopvq_status_string.restype = [_I32], ctypes.c_char_p
@@ -260,20 +262,38 @@ def loopvq_decode_attn_workspace(cfg, batch: int, max_seq_len: int) -> int:
     return n.value
 
 
+def _decode_args(layer, loop, batch, q, seq_lens, max_seq_len, out, block_table, pool, max_pages_per_seq,
+                 num_pages, cb_k_prep, cb_v_prep, k_prefix, v_prefix, k_recent, v_recent, rot, softmax_scale, lse,
+                 num_splits):
+    return loopvq_decode_args(layer=layer, loop=loop, batch=batch, max_pages_per_seq=max_pages_per_seq,
+                              max_seq_len=max_seq_len, num_splits=num_splits, num_pages=num_pages, q=_ptr(q),
+                              seq_lens=_ptr(seq_lens), block_table=_ptr(block_table), pool=_ptr(pool),
+                              cb_k_prep=_ptr(cb_k_prep), cb_v_prep=_ptr(cb_v_prep), k_prefix=_ptr(k_prefix),
+                              v_prefix=_ptr(v_prefix), k_recent=_ptr(k_recent), v_recent=_ptr(v_recent),
+                              rot=_ptr(rot), softmax_scale=softmax_scale, out=_ptr(out), lse=_ptr(lse))
+
+
 def loopvq_decode_attn(cfg, *, layer, loop, batch, q, seq_lens, max_seq_len, out, block_table=None, pool=None,
                        max_pages_per_seq=0, num_pages=0, cb_k_prep=None, cb_v_prep=None, k_prefix=None,
                        v_prefix=None, k_recent=None, v_recent=None, rot=None, softmax_scale=0.0, lse=None,
                        num_splits=0, workspace=None, workspace_bytes=None, stream=None) -> None:
-    a = loopvq_decode_args(layer=layer, loop=loop, batch=batch, max_pages_per_seq=max_pages_per_seq,
-                           max_seq_len=max_seq_len, num_splits=num_splits, num_pages=num_pages, q=_ptr(q),
-                           seq_lens=_ptr(seq_lens), block_table=_ptr(block_table), pool=_ptr(pool),
-                           cb_k_prep=_ptr(cb_k_prep), cb_v_prep=_ptr(cb_v_prep), k_prefix=_ptr(k_prefix),
-                           v_prefix=_ptr(v_prefix), k_recent=_ptr(k_recent), v_recent=_ptr(v_recent),
-                           rot=_ptr(rot), softmax_scale=softmax_scale, out=_ptr(out), lse=_ptr(lse))
+    a = _decode_args(layer, loop, batch, q, seq_lens, max_seq_len, out, block_table, pool, max_pages_per_seq,
+                     num_pages, cb_k_prep, cb_v_prep, k_prefix, v_prefix, k_recent, v_recent, rot, softmax_scale, lse,
+                     num_splits)
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().loopvq_decode_attn(ctypes.byref(cfg), ctypes.byref(a), _ptr(workspace), workspace_bytes,
                                     _stream(stream)))
+
+
+def loopvq_decode_attn_noalloc(cfg, *, layer, loop, batch, q, seq_lens, max_seq_len, out, block_table=None,
+                               pool=None, max_pages_per_seq=0, num_pages=0, cb_k_prep=None, cb_v_prep=None,
+                               k_prefix=None, v_prefix=None, k_recent=None, v_recent=None, rot=None,
+                               softmax_scale=0.0, lse=None, num_splits=0, stream=None) -> None:
+    a = _decode_args(layer, loop, batch, q, seq_lens, max_seq_len, out, block_table, pool, max_pages_per_seq,
+                     num_pages, cb_k_prep, cb_v_prep, k_prefix, v_prefix, k_recent, v_recent, rot, softmax_scale, lse,
+                     num_splits)
+    _check(lib().loopvq_decode_attn_noalloc(ctypes.byref(cfg), ctypes.byref(a), _stream(stream)))
 
 
 def loopvq_extend_attn(cfg, *, layer, loop, batch, chunk, q, k_new, v_new, seq_lens, max_seq_len, out,

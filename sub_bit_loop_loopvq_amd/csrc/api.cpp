@@ -194,6 +194,98 @@ loopvq_status check_lloyd(const loopvq_config* cfg, const loopvq_lloyd_args* a) 
   return LOOPVQ_OK;
 }
 
+// Checks of a decode call (every one before any HIP call) and its launch parameters; the split
+// workspace is the caller's business: *need bytes of it, placed in p->ws.
+loopvq_status decode_setup(const loopvq_config* cfg, const loopvq_decode_args* a, lvq::DecodeParams* out,
+                           size_t* need_out) {
+  loopvq_status s = check_config(cfg);
+  if (s) return s;
+  if (!a) return fail(LOOPVQ_ERR_INVALID_ARG, "args is NULL");
+  if ((s = check_supported(cfg))) return s;
+  const Sizes z = sizes_of(cfg);
+  if (a->layer < 0 || a->layer >= cfg->num_layers) return fail(LOOPVQ_ERR_INVALID_ARG, "layer out of range");
+  if (a->loop < 0 || a->loop >= cfg->num_loops) return fail(LOOPVQ_ERR_INVALID_ARG, "loop out of range");
+  if (a->batch < 1) return fail(LOOPVQ_ERR_INVALID_ARG, "batch must be >= 1");
+  if (a->max_seq_len < 1) return fail(LOOPVQ_ERR_INVALID_ARG, "max_seq_len must be >= 1");
+  if (a->num_splits < 0 || a->num_splits > 256) return fail(LOOPVQ_ERR_INVALID_ARG, "num_splits must be in [0, 256]");
+  if (int64_t(a->batch) * cfg->num_q_heads * 256 > (int64_t(1) << 31) - 1)
+    return fail(LOOPVQ_ERR_INVALID_ARG, "batch * num_q_heads too large");
+  if (!a->q || !a->seq_lens || !a->out) return fail(LOOPVQ_ERR_INVALID_ARG, "q, seq_lens and out must not be NULL");
+  const bool can_vq = int64_t(a->max_seq_len) > int64_t(cfg->prefix_tokens) + cfg->recent_tokens;
+  if (can_vq) {
+    if (!a->block_table || !a->pool || !a->cb_k_prep || !a->cb_v_prep)
+      return fail(LOOPVQ_ERR_INVALID_ARG, "block_table, pool and prepared codebooks must not be NULL");
+    if (a->max_pages_per_seq < 1 || a->num_pages < 1)
+      return fail(LOOPVQ_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
+    if (!aligned(a->pool, 16) || !aligned(a->cb_k_prep, 16) || !aligned(a->cb_v_prep, 16))
+      return fail(LOOPVQ_ERR_MISALIGNED, "pool and prepared codebooks must be 16-byte aligned");
+  }
+  if (cfg->prefix_tokens > 0 && (!a->k_prefix || !a->v_prefix))
+    return fail(LOOPVQ_ERR_INVALID_ARG, "prefix windows must not be NULL when prefix_tokens > 0");
+  if (cfg->recent_tokens > 0 && (!a->k_recent || !a->v_recent))
+    return fail(LOOPVQ_ERR_INVALID_ARG, "recent windows must not be NULL when recent_tokens > 0");
+  if ((a->k_prefix && !aligned(a->k_prefix, 16)) || (a->v_prefix && !aligned(a->v_prefix, 16)) ||
+      (a->k_recent && !aligned(a->k_recent, 16)) || (a->v_recent && !aligned(a->v_recent, 16)))
+    return fail(LOOPVQ_ERR_MISALIGNED, "window buffers must be 16-byte aligned");
+  if (!aligned(a->q, 2) || !aligned(a->out, 4) || (a->lse && !aligned(a->lse, 4)) || (a->rot && !aligned(a->rot, 4)) ||
+      !aligned(a->seq_lens, 4))
+    return fail(LOOPVQ_ERR_MISALIGNED, "q, out, lse, rot or seq_lens misaligned");
+  const int S = a->num_splits > 0 ? a->num_splits : plan_splits(cfg, a->batch, a->max_seq_len);
+  if (S < min_splits(cfg, a->max_seq_len) || S > 256)
+    return fail(LOOPVQ_ERR_INVALID_ARG, "num_splits %d: a context of %d tokens needs between %d and 256 splits", S,
+                a->max_seq_len, min_splits(cfg, a->max_seq_len));
+  if (can_vq && int64_t(a->max_seq_len) - cfg->prefix_tokens - cfg->recent_tokens >
+                    int64_t(a->max_pages_per_seq) * cfg->page_tokens)
+    return fail(LOOPVQ_ERR_INVALID_ARG,
+                "max_pages_per_seq (%d) pages of %d tokens cannot hold the %lld vector-quantized tokens of "
+                "max_seq_len %d", a->max_pages_per_seq, cfg->page_tokens,
+                (long long)(int64_t(a->max_seq_len) - cfg->prefix_tokens - cfg->recent_tokens), a->max_seq_len);
+  if (can_vq && int64_t(a->num_pages) * z.page_bytes > INT32_MAX)
+    return fail(LOOPVQ_ERR_UNSUPPORTED, "num_pages * page_bytes (one kv-head's page region) must stay below 2 GiB");
+  const int64_t Q = int64_t(a->batch) * cfg->num_q_heads;
+  *need_out = S > 1 ? size_t(S) * Q * (cfg->head_dim + 4) * sizeof(float) : 0;
+
+  const int j = a->loop / cfg->loop_group;
+  const int jcb = cfg->codebook_per_loop_group ? j : 0;
+  lvq::DecodeParams p{};
+  p.B = a->batch;
+  p.Hq = cfg->num_q_heads;
+  p.Hkv = cfg->num_kv_heads;
+  p.d = cfg->head_dim;
+  p.P = cfg->prefix_tokens;
+  p.R = cfg->recent_tokens;
+  p.G = cfg->loop_group;
+  p.pt_shift = ilog2(cfg->page_tokens);
+  p.max_pages = can_vq ? a->max_pages_per_seq : 0;
+  p.max_seq_len = a->max_seq_len;
+  p.S = S;
+  p.tau = a->loop % cfg->loop_group;
+  p.num_pages = a->num_pages;
+  p.page_bytes = z.page_bytes;
+  p.kind_bytes = z.kind_bytes;
+  const float scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / std::sqrt(float(cfg->head_dim));
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.q = a->q;
+  p.seq_lens = a->seq_lens;
+  p.block_table = a->block_table;
+  p.head_stride = a->num_pages * z.page_bytes;
+  p.pool_lj = can_vq ? a->pool + (int64_t(a->layer) * z.J + j) * cfg->num_kv_heads * p.head_stride : nullptr;
+  const int64_t set0 = (int64_t(a->layer) * z.Jcb + jcb) * cfg->num_kv_heads;
+  const int64_t set_elems = int64_t(cfg->loop_group) * z.K * cfg->head_dim;
+  p.cbk = can_vq ? a->cb_k_prep + set0 * set_elems : nullptr;
+  p.cbv = can_vq ? a->cb_v_prep + set0 * set_elems : nullptr;
+  p.k_prefix = a->k_prefix;
+  p.v_prefix = a->v_prefix;
+  p.k_recent = a->k_recent;
+  p.v_recent = a->v_recent;
+  p.rot = a->rot;
+  p.out = a->out;
+  p.lse = a->lse;
+  p.ws = nullptr;
+  *out = p;
+  return LOOPVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -456,95 +548,38 @@ loopvq_status loopvq_decode_attn_workspace(const loopvq_config* cfg, int32_t bat
 
 loopvq_status loopvq_decode_attn(const loopvq_config* cfg, const loopvq_decode_args* a, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-  loopvq_status s = check_config(cfg);
+  lvq::DecodeParams p;
+  size_t need = 0;
+  const loopvq_status s = decode_setup(cfg, a, &p, &need);
   if (s) return s;
-  if (!a) return fail(LOOPVQ_ERR_INVALID_ARG, "args is NULL");
-  if ((s = check_supported(cfg))) return s;
-  const Sizes z = sizes_of(cfg);
-  if (a->layer < 0 || a->layer >= cfg->num_layers) return fail(LOOPVQ_ERR_INVALID_ARG, "layer out of range");
-  if (a->loop < 0 || a->loop >= cfg->num_loops) return fail(LOOPVQ_ERR_INVALID_ARG, "loop out of range");
-  if (a->batch < 1) return fail(LOOPVQ_ERR_INVALID_ARG, "batch must be >= 1");
-  if (a->max_seq_len < 1) return fail(LOOPVQ_ERR_INVALID_ARG, "max_seq_len must be >= 1");
-  if (a->num_splits < 0 || a->num_splits > 256) return fail(LOOPVQ_ERR_INVALID_ARG, "num_splits must be in [0, 256]");
-  if (int64_t(a->batch) * cfg->num_q_heads * 256 > (int64_t(1) << 31) - 1)
-    return fail(LOOPVQ_ERR_INVALID_ARG, "batch * num_q_heads too large");
-  if (!a->q || !a->seq_lens || !a->out) return fail(LOOPVQ_ERR_INVALID_ARG, "q, seq_lens and out must not be NULL");
-  const bool can_vq = int64_t(a->max_seq_len) > int64_t(cfg->prefix_tokens) + cfg->recent_tokens;
-  if (can_vq) {
-    if (!a->block_table || !a->pool || !a->cb_k_prep || !a->cb_v_prep)
-      return fail(LOOPVQ_ERR_INVALID_ARG, "block_table, pool and prepared codebooks must not be NULL");
-    if (a->max_pages_per_seq < 1 || a->num_pages < 1)
-      return fail(LOOPVQ_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
-    if (!aligned(a->pool, 16) || !aligned(a->cb_k_prep, 16) || !aligned(a->cb_v_prep, 16))
-      return fail(LOOPVQ_ERR_MISALIGNED, "pool and prepared codebooks must be 16-byte aligned");
-  }
-  if (cfg->prefix_tokens > 0 && (!a->k_prefix || !a->v_prefix))
-    return fail(LOOPVQ_ERR_INVALID_ARG, "prefix windows must not be NULL when prefix_tokens > 0");
-  if (cfg->recent_tokens > 0 && (!a->k_recent || !a->v_recent))
-    return fail(LOOPVQ_ERR_INVALID_ARG, "recent windows must not be NULL when recent_tokens > 0");
-  if ((a->k_prefix && !aligned(a->k_prefix, 16)) || (a->v_prefix && !aligned(a->v_prefix, 16)) ||
-      (a->k_recent && !aligned(a->k_recent, 16)) || (a->v_recent && !aligned(a->v_recent, 16)))
-    return fail(LOOPVQ_ERR_MISALIGNED, "window buffers must be 16-byte aligned");
-  if (!aligned(a->q, 2) || !aligned(a->out, 4) || (a->lse && !aligned(a->lse, 4)) || (a->rot && !aligned(a->rot, 4)) ||
-      !aligned(a->seq_lens, 4))
-    return fail(LOOPVQ_ERR_MISALIGNED, "q, out, lse, rot or seq_lens misaligned");
-  const int S = a->num_splits > 0 ? a->num_splits : plan_splits(cfg, a->batch, a->max_seq_len);
-  if (S < min_splits(cfg, a->max_seq_len) || S > 256)
-    return fail(LOOPVQ_ERR_INVALID_ARG, "num_splits %d: a context of %d tokens needs between %d and 256 splits", S,
-                a->max_seq_len, min_splits(cfg, a->max_seq_len));
-  if (can_vq && int64_t(a->max_seq_len) - cfg->prefix_tokens - cfg->recent_tokens >
-                    int64_t(a->max_pages_per_seq) * cfg->page_tokens)
-    return fail(LOOPVQ_ERR_INVALID_ARG,
-                "max_pages_per_seq (%d) pages of %d tokens cannot hold the %lld vector-quantized tokens of "
-                "max_seq_len %d", a->max_pages_per_seq, cfg->page_tokens,
-                (long long)(int64_t(a->max_seq_len) - cfg->prefix_tokens - cfg->recent_tokens), a->max_seq_len);
-  if (can_vq && int64_t(a->num_pages) * z.page_bytes > INT32_MAX)
-    return fail(LOOPVQ_ERR_UNSUPPORTED, "num_pages * page_bytes (one kv-head's page region) must stay below 2 GiB");
-  const int64_t Q = int64_t(a->batch) * cfg->num_q_heads;
-  const size_t need = S > 1 ? size_t(S) * Q * (cfg->head_dim + 4) * sizeof(float) : 0;
   if (workspace_bytes < need || (need && !workspace))
-    return fail(LOOPVQ_ERR_WORKSPACE, "workspace too small: %zu bytes needed for %d splits", need, S);
+    return fail(LOOPVQ_ERR_WORKSPACE, "workspace too small: %zu bytes needed for %d splits", need, p.S);
   if (need && !aligned(workspace, 16)) return fail(LOOPVQ_ERR_MISALIGNED, "workspace must be 16-byte aligned");
-
-  const int j = a->loop / cfg->loop_group;
-  const int jcb = cfg->codebook_per_loop_group ? j : 0;
-  lvq::DecodeParams p{};
-  p.B = a->batch;
-  p.Hq = cfg->num_q_heads;
-  p.Hkv = cfg->num_kv_heads;
-  p.d = cfg->head_dim;
-  p.P = cfg->prefix_tokens;
-  p.R = cfg->recent_tokens;
-  p.G = cfg->loop_group;
-  p.pt_shift = ilog2(cfg->page_tokens);
-  p.max_pages = can_vq ? a->max_pages_per_seq : 0;
-  p.max_seq_len = a->max_seq_len;
-  p.S = S;
-  p.tau = a->loop % cfg->loop_group;
-  p.num_pages = a->num_pages;
-  p.page_bytes = z.page_bytes;
-  p.kind_bytes = z.kind_bytes;
-  const float scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / std::sqrt(float(cfg->head_dim));
-  p.scale_log2 = scale * 1.4426950408889634f;
-  p.q = a->q;
-  p.seq_lens = a->seq_lens;
-  p.block_table = a->block_table;
-  p.head_stride = a->num_pages * z.page_bytes;
-  p.pool_lj = can_vq ? a->pool + (int64_t(a->layer) * z.J + j) * cfg->num_kv_heads * p.head_stride : nullptr;
-  const int64_t set0 = (int64_t(a->layer) * z.Jcb + jcb) * cfg->num_kv_heads;
-  const int64_t set_elems = int64_t(cfg->loop_group) * z.K * cfg->head_dim;
-  p.cbk = can_vq ? a->cb_k_prep + set0 * set_elems : nullptr;
-  p.cbv = can_vq ? a->cb_v_prep + set0 * set_elems : nullptr;
-  p.k_prefix = a->k_prefix;
-  p.v_prefix = a->v_prefix;
-  p.k_recent = a->k_recent;
-  p.v_recent = a->v_recent;
-  p.rot = a->rot;
-  p.out = a->out;
-  p.lse = a->lse;
   p.ws = static_cast<float*>(workspace);
-  const hipError_t e = lvq::launch_decode(p, z.ng, cfg->chans_per_group, (hipStream_t)stream);
+  const hipError_t e = lvq::launch_decode(p, cfg->head_dim / cfg->chans_per_group, cfg->chans_per_group,
+                                          (hipStream_t)stream);
   if (e != hipSuccess) return fail(LOOPVQ_ERR_HIP, "decode_attn launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+loopvq_status loopvq_decode_attn_noalloc(const loopvq_config* cfg, const loopvq_decode_args* a, void* stream) {
+  lvq::DecodeParams p;
+  size_t need = 0;
+  const loopvq_status s = decode_setup(cfg, a, &p, &need);
+  if (s) return s;
+  if (need > lvq::kDecodeStaticScratchBytes)
+    return fail(LOOPVQ_ERR_WORKSPACE,
+                "the split plan (%d splits) needs %zu bytes of partials; the static scratch holds %zu bytes", p.S,
+                need, lvq::kDecodeStaticScratchBytes);
+  if (need) {
+    void* ws = nullptr;
+    const hipError_t e = lvq::decode_static_scratch(&ws);
+    if (e != hipSuccess) return fail(LOOPVQ_ERR_HIP, "static decode scratch lookup: %s", hipGetErrorString(e));
+    p.ws = static_cast<float*>(ws);
+  }
+  const hipError_t e = lvq::launch_decode(p, cfg->head_dim / cfg->chans_per_group, cfg->chans_per_group,
+                                          (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LOOPVQ_ERR_HIP, "decode_attn_noalloc launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -46,7 +46,14 @@
 
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
+
+// Split partials of loopvq_decode_attn_noalloc: one copy of this array lives on every GPU the
+// library runs on, from module load to process end.  In host code `scratch` names a host-side
+// stand-in, never the device memory: host code only uses the address hipGetSymbolAddress
+// returns for the current device (lvq::decode_static_scratch).
+static __device__ __align__(256) uint8_t scratch[lvq::kDecodeStaticScratchBytes];
 
 namespace lvq {
 namespace {
@@ -721,6 +728,26 @@ hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t decode_static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));   // with device `dev` current
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeParams& p, int ng, int c, hipStream_t stream) {
   if (ng == 32 && c == 4) return launch_variant<32, 4>(p, stream);

@@ -123,6 +123,12 @@ hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream);
 hipError_t launch_prepare_groups(const PrepareParams& p, hipStream_t stream);
 hipError_t launch_lloyd(const LloydParams& p, int c, hipStream_t stream);
 
+// The decode split workspace for callers that cannot allocate: a static device array of
+// kDecodeStaticScratchBytes per GPU.  decode_static_scratch() returns its address on the
+// current device (looked up once per device, then cached).
+constexpr size_t kDecodeStaticScratchBytes = size_t(16) << 20;
+hipError_t decode_static_scratch(void** ptr);
+
 // ---------------------------------------------------------------------------
 // Device helpers
 // ---------------------------------------------------------------------------

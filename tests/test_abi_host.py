@@ -200,6 +200,25 @@ def test_decode_rejects_a_page_region_of_2_gib():
     assert e.value.status == lvq.LOOPVQ_ERR_WORKSPACE
 
 
+
+def test_decode_noalloc_refuses_a_plan_beyond_the_static_array():
+    """The allocation-free decode refuses, before any HIP call, a split plan whose partials exceed
+    its static per-GPU array; up to that size it checks exactly what the workspace entry point checks."""
+    wl = W.LAYER_4K.with_(batch=128)
+    cfg = lvq.make_config(wl)
+    assert 256 * wl.batch * wl.q_heads * (wl.head_dim + 4) * 4 > 16 << 20
+    kw = _decode_kw(wl, num_splits=256, max_pages_per_seq=64)
+    kw.pop("workspace"), kw.pop("workspace_bytes")
+    with pytest.raises(lvq.LoopVQError) as e:
+        lvq.loopvq_decode_attn_noalloc(cfg, **kw)
+    assert e.value.status == lvq.LOOPVQ_ERR_WORKSPACE
+    assert "static scratch" in lvq.loopvq_last_error()
+    for over, status in ((dict(layer=1), lvq.LOOPVQ_ERR_INVALID_ARG), (dict(pool=FAKE + 8), lvq.LOOPVQ_ERR_MISALIGNED),
+                         (dict(num_splits=300), lvq.LOOPVQ_ERR_INVALID_ARG)):
+        with pytest.raises(lvq.LoopVQError) as e:
+            lvq.loopvq_decode_attn_noalloc(cfg, **dict(kw, **over))
+        assert e.value.status == status
+
 def test_unsupported_variants_rejected():
     for over in [dict(index_bits=9), dict(loop_group=2, num_loops=4), dict(chans_per_group=8, head_dim=256),
                  dict(loop_group=8, num_loops=8, chans_per_group=8)]:
