@@ -337,8 +337,18 @@ class Bf16Bench:
                     self.decode(l, t)
 
 
+def host_cores() -> dict:
+    """What the host offers the CPU baseline: logical CPUs, the ones this process may run on, and the
+    BLAS pool's default thread count (the baseline itself pins BLAS to one thread)."""
+    from threadpoolctl import threadpool_info
+    blas = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+    return {"host_cpus": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0)),
+            "blas_threads_default": max(blas) if blas else None}
+
+
 def cpu_baseline(wl, seconds: float) -> dict:
-    """The CPU oracle (fp64, single BLAS thread) on sampled decode queries of the same workload."""
+    """The CPU oracle (fp64, single BLAS thread) on sampled decode queries of the same workload, with
+    generator indices (the workloads whose GPU pool is not one Bench pool: --plan, --bf16-cache)."""
     from threadpoolctl import threadpool_limits
     from oracle import loopvq_oracle as O
     from synth import gen
@@ -373,10 +383,74 @@ def cpu_baseline(wl, seconds: float) -> dict:
             done += 1
             if busy >= seconds:
                 break
-    return {"value": done / busy, "unit": "queries/s", "cores": 1, "kind": "oracle",
+    return {"value": done / busy, "unit": "queries/s", "cores": 1, "kind": "oracle", **host_cores(),
             "sample": (f"{done} decode queries (layer 0, loop step 0, sequences 0..{(done - 1) // wl.q_heads}) at "
-                       f"full context {wl.context}: unpack packed pages + dequantize + fp64 softmax attention; "
-                       f"{busy:.1f}s of timed oracle work, 1 BLAS thread; input setup untimed "
+                       f"full context {wl.context}: unpack packed pages (generator indices) + dequantize + fp64 "
+                       f"softmax attention; {busy:.1f}s of timed oracle work, 1 BLAS thread; input setup untimed "
+                       f"(wall {time.time() - t_start:.1f}s)")}
+
+
+def cpu_baseline_gpu_pages(bench, seconds: float) -> dict:
+    """The CPU oracle (fp64, one BLAS thread) on sampled decode queries of (layer 0, loop step 0), fed
+    with exactly what the GPU decodes: the packed pages the GPU encode wrote (copied back through the
+    block table), the bf16 windows, queries and codebooks in HBM.  The GPU's own output for the same
+    launch is compared with the oracle's on the sampled queries (rel-L2 and max-abs)."""
+    import torch
+    from threadpoolctl import threadpool_limits
+    from oracle import loopvq_oracle as O
+    from synth import gen
+    t_start = time.time()
+    wl, lvq = bench.wl, bench.lvq
+    l, t = 0, 0
+    j, tau = t // wl.loop_group, t % wl.loop_group
+    jc = j if wl.codebook_per_loop_group else 0
+    # the GPU's output of this launch, over the same pool the oracle reads
+    out = torch.empty_like(bench.out)
+    lvq.loopvq_decode_attn(bench.cfg, layer=l, loop=t, batch=wl.batch, q=bench.q[l, t], seq_lens=bench.lens,
+                           max_seq_len=wl.context, out=out, block_table=bench.bt, pool=bench.pool,
+                           max_pages_per_seq=bench.pages_per_seq, num_pages=bench.num_pages,
+                           cb_k_prep=bench.prep[0], cb_v_prep=bench.prep[1], k_prefix=bench.pre[0, l, t],
+                           v_prefix=bench.pre[1, l, t], k_recent=bench.rec[0, l, t], v_recent=bench.rec[1, l, t],
+                           rot=bench.rot, workspace=bench.ws, workspace_bytes=bench.ws_bytes)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().astype(np.float64)
+    u16 = lambda x: x.cpu().numpy().view(np.uint16)   # noqa: E731
+    q = u16(bench.q[l, t])
+    cb = {k: gen.bf16_to_f64(u16(bench.cb[k][l, jc])) for k in (0, 1)}          # [H][NG][K][E]
+    bt = bench.bt.cpu().numpy()
+    rot = bench.rot.cpu().numpy().astype(np.float64) if bench.rot is not None else None
+    n_pre, n_vq, n_rec = O.split_context(wl.context, wl.prefix, wl.recent)
+    grp = wl.q_heads // wl.kv_heads
+    page_bytes = bench.lay.page_bytes
+    n_pages = -(-n_vq // wl.page_tokens)
+    done, busy, rel, mx = 0, 0.0, 0.0, 0.0
+    with threadpool_limits(limits=1):
+        for qi in range(wl.batch * wl.q_heads):
+            b, hq = divmod(qi, wl.q_heads)
+            h = hq // grp
+            offs = [O.pool_offset(l, j, h, int(bt[b, pg]), wl.loop_groups, wl.kv_heads, bench.num_pages, page_bytes)
+                    for pg in range(n_pages)]
+            idx = torch.tensor(offs, dtype=torch.int64, device=bench.pool.device)[:, None] + \
+                torch.arange(page_bytes, device=bench.pool.device)[None]
+            pages = bench.pool[idx].cpu().numpy()                              # [n_pages][page_bytes]
+            win = [gen.bf16_to_f64(u16(a[kind, l, t, b, h, :n])) for kind in (0, 1)
+                   for a, n in ((bench.pre, n_pre), (bench.rec, n_rec))]       # kp, kr, vp, vr
+            c0 = time.perf_counter()
+            ik, iv = O.unpack_sequence(pages, n_vq, wl.groups, wl.page_tokens, wl.index_bits)
+            o, _ = O.decode_query(gen.bf16_to_f64(q[b, hq]), win[0], win[2], ik, iv, cb[0][h], cb[1][h], win[1],
+                                  win[3], tau, wl.chans, 1.0 / np.sqrt(wl.head_dim), rot)
+            busy += time.perf_counter() - c0
+            rel = max(rel, float(np.linalg.norm(out[b, hq] - o) / max(np.linalg.norm(o), 1e-30)))
+            mx = max(mx, float(np.abs(out[b, hq] - o).max()))
+            done += 1
+            if busy >= seconds:
+                break
+    return {"value": done / busy, "unit": "queries/s", "cores": 1, "kind": "oracle", **host_cores(),
+            "gpu_vs_oracle": {"queries": done, "rel_l2_max": rel, "max_abs": mx},
+            "sample": (f"{done} decode queries (layer 0, loop step 0, sequences 0..{(done - 1) // wl.q_heads}) at "
+                       f"full context {wl.context}, on the GPU's own inputs copied back (the packed pages its "
+                       f"encode wrote, bf16 windows, queries, codebooks): unpack + dequantize + fp64 softmax "
+                       f"attention; {busy:.1f}s of timed oracle work, 1 BLAS thread; copies untimed "
                        f"(wall {time.time() - t_start:.1f}s)")}
 
 
@@ -461,7 +535,7 @@ def encode_cpu_baseline(wl, seconds: float, layer=0, loop_group=0, kind=0) -> di
                     break
             if busy >= seconds:
                 break
-    return {"value": done / busy, "unit": "sub-vectors/s", "cores": 1, "kind": "oracle",
+    return {"value": done / busy, "unit": "sub-vectors/s", "cores": 1, "kind": "oracle", **host_cores(),
             "sample": (f"{done} sub-vectors ({rows} (token, kv-head) rows of sequence 0 x {wl.groups} groups) of "
                        f"layer {layer}, loop group {loop_group}, kind {kind}: brute-force fp64 distances to all "
                        f"{wl.codewords} codewords + argmin; {busy:.1f}s of timed oracle work, 1 BLAS thread; input "
@@ -622,6 +696,7 @@ def extend_cpu_baseline(wl, chunk, seconds: float) -> dict:
                 break
     vis = wl.context + chunk
     return {"value": rows * 4.0 * wl.head_dim * vis / busy / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            **host_cores(),
             "sample": (f"{rows} chunk rows (the last 8 of a {chunk}-row chunk, sequences 0..{rows // 8 - 1}) over "
                        f"the full {wl.context}-token cache: unpack + dequantize + fp64 softmax attention, "
                        f"{busy:.1f}s of timed oracle work, 1 BLAS thread; input setup untimed "
@@ -746,7 +821,7 @@ def lloyd_cpu_baseline(wl, seconds: float, layer=0, loop_group=0, kind=0) -> dic
             groups += 1
             if busy >= seconds:
                 break
-    return {"value": done / busy, "unit": "sub-vectors/s", "cores": 1, "kind": "oracle",
+    return {"value": done / busy, "unit": "sub-vectors/s", "cores": 1, "kind": "oracle", **host_cores(),
             "sample": (f"{groups} whole (kv-head 0, group) sample sets of {n} sub-vectors each of layer {layer}, "
                        f"loop group {loop_group}, kind {kind}: one weighted Lloyd iteration each (fp64 brute-force "
                        f"assignment over {wl.codewords} codewords, weighted means, bf16 rounding); {busy:.1f}s of "
@@ -969,8 +1044,11 @@ def main():
         rec["graph"] = graph
     if not args.no_cpu_baseline:
         # with a plan: the oracle on the workload of layer 0's first segment
-        base = wl.with_(chans=plan[0][0][1], loop_group=plan[0][0][2]) if plan else wl
-        rec["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
+        if plan or args.bf16_cache:
+            base = wl.with_(chans=plan[0][0][1], loop_group=plan[0][0][2]) if plan else wl
+            rec["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
+        else:
+            rec["cpu_baseline"] = cpu_baseline_gpu_pages(bench, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
 
 
