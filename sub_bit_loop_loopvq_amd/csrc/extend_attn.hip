@@ -60,16 +60,17 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
   constexpr int KROW = D + 8;         // bf16 per K row (16 B of padding)
   constexpr int KSTEPS = D / 16;      // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;          // 32-channel blocks of O^T
-  // Without a rotation the q operand lives in LDS (each wave reads back only its own rows), which
-  // frees the registers that hold the next tile's keys and values while this one is consumed.
-  constexpr bool QL = !ROT;
-  constexpr int QROW = D + 8;         // bf16 per q row (16 B of padding)
-  // K / V^T tiles: two buffers without a rotation (tile k + 1 is staged while tile k is consumed)
-  __shared__ __align__(16) uint16_t ks2[QL ? 2 : 1][kKT * KROW];
-  __shared__ __align__(16) uint16_t vt2[QL ? 2 : 1][D * kVRow];
+  // Without a rotation: two K / V^T tile buffers (tile k + 1 is staged while tile k is consumed)
+  // and the key codebook's loop-step slice of the kv-head in LDS (its K x d bf16, loaded once), so
+  // that the dequantization of vector-quantized keys gathers from LDS instead of L2; q stays in
+  // registers.
+  constexpr bool DBUF = !ROT;
+  constexpr bool CBL = !ROT;
+  __shared__ __align__(16) uint16_t ks2[DBUF ? 2 : 1][kKT * KROW];
+  __shared__ __align__(16) uint16_t vt2[DBUF ? 2 : 1][D * kVRow];
+  __shared__ __align__(16) uint16_t cbk_l[CBL ? kCodes * D : 8];
   uint16_t* ks = ks2[0];
   uint16_t* vt = vt2[0];
-  __shared__ __align__(16) uint16_t qs[QL ? kRows * QROW : 8];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -123,13 +124,8 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
   } else {
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * half);
-      if constexpr (QL) {
-        *reinterpret_cast<u32x4*>(qs + (wave * 32 + col) * QROW + 16 * kk + 8 * half) = v;
-      } else {
-        bq[kk] = v;
-        bq_lo[kk] = u32x4{0u, 0u, 0u, 0u};
-      }
+      bq[kk] = *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * half);
+      bq_lo[kk] = u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -215,7 +211,7 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
         for (int r = 0; r < 4; ++r) {
           const int g = 4 * gq + r;
           const uint32_t kx = (ik[m] >> (8 * r)) & 0xffu, vx = (iv[m] >> (8 * r)) & 0xffu;
-          const uint32_t* kc = reinterpret_cast<const uint32_t*>(slice_k + (g * kCodes + kx) * C);
+          const uint32_t* kc = reinterpret_cast<const uint32_t*>((CBL ? cbk_l : slice_k) + (g * kCodes + kx) * C);
           const uint32_t* vc = reinterpret_cast<const uint32_t*>(slice_v + (g * kCodes + vx) * C);
 #pragma unroll
           for (int e = 0; e < C / 2; ++e) {
@@ -302,9 +298,7 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
       f32x16 acc = {};
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
-        const u32x4 qb = QL ? *reinterpret_cast<const u32x4*>(qs + (wave * 32 + col) * QROW + 16 * kk + 8 * half)
-                            : bq[kk];
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[kk]), as_bf16x8(qb), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[kk]), as_bf16x8(bq[kk]), acc, 0, 0, 0);
         if constexpr (ROT)
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[kk]), as_bf16x8(bq_lo[kk]), acc, 0, 0, 0);
       }
@@ -382,8 +376,18 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
   };
 
   // ---- the key tiles ------------------------------------------------------------------------------
+  if constexpr (CBL) {
+    if (t_vq > 0) {   // (uniform) the key codebook slice into LDS, 16 B per thread and step
+      constexpr int PER = kCodes * D * 2 / 16 / NTH;
+      static_assert(PER * NTH * 16 == kCodes * D * 2, "codebook staging");
+#pragma unroll
+      for (int m = 0; m < PER; ++m)
+        reinterpret_cast<u32x4*>(cbk_l)[tid + NTH * m] = reinterpret_cast<const u32x4*>(slice_k)[tid + NTH * m];
+      __syncthreads();
+    }
+  }
   fetch_idx(0, ik_n, iv_n, ok_n);
-  if constexpr (QL) {
+  if constexpr (DBUF) {
     // tile k + 1's keys and values load while tile k is consumed
     // two LDS buffers: tile k + 1 is stored, and tile k + 2 loaded into registers, while tile k
     // is consumed; one barrier per tile
