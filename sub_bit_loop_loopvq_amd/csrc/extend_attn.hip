@@ -33,11 +33,35 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kKT = 64;        // keys per tile
 constexpr int kVRow = kKT + 4; // bf16 per transposed V row (8 B of padding)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
+// two fp32 -> packed fp16, round to nearest even
+__device__ __forceinline__ uint32_t f16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+// two packed bf16 -> packed fp16 (exact inside the window below)
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) { return f16x2_rne(bf16_lo(w), bf16_hi(w)); }
+// The fp16 window: a bf16 value converts to fp16 exactly when it is zero or its magnitude lies in
+// [2^-17, 2^16) (8 significant bits need an exponent of at least -17 in fp16, whose subnormals
+// reach 2^-24; 2^16 overflows).  Magnitude bits of bf16 compare like the magnitudes; bf16
+// infinities and NaNs lie above kF16Hi.
+constexpr uint32_t kF16Hi = (127u + 16u) << 7;    // 2^16
+constexpr uint32_t kF16Lo = (127u - 17u) << 7;    // 2^-17
+// running packed statistics of the magnitude bits m of two bf16: the maximum, and the minimum
+// of m - 1 (wrapping, so zeros count as 0xffff and never as small)
+__device__ __forceinline__ void mag_stats(uint32_t& mx, uint32_t& mn1, uint32_t w) {
+  const u16x2 m = __builtin_bit_cast(u16x2, w & 0x7fff7fffu);
+  mx = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, mx), m));
+  mn1 = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, mn1), m - (unsigned short)1));
+}
 
 // round-to-nearest-even fp32 -> bf16 bits (finite inputs)
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
@@ -69,6 +93,12 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
   __shared__ __align__(16) uint16_t ks2[DBUF ? 2 : 1][kKT * KROW];
   __shared__ __align__(16) uint16_t vt2[DBUF ? 2 : 1][D * kVRow];
   __shared__ __align__(16) uint16_t cbk_l[CBL ? kCodes * D : 8];
+  // Without a rotation the value tiles are staged as fp16 and the value product runs on fp16
+  // MFMAs with P rounded to fp16: one product instead of the bf16 hi + lo pair.  The first tile
+  // with a value outside the fp16 window ends that loop; a second loop, in bf16, goes on from it.
+  constexpr bool F16 = !ROT;
+  constexpr int NWAVE = NTH / 64;
+  __shared__ uint32_t vbad[2][NWAVE];   // per buffer and wave: a value outside the fp16 window
   uint16_t* ks = ks2[0];
   uint16_t* vt = vt2[0];
 
@@ -97,6 +127,8 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
 
   // ---- this lane's query row and its q operand (B of S^T = K Q^T) --------------------------
   const int row = row_ws + wave * 32 + col;
+  // the wave's last chunk token: a chunk tile that starts after it is hidden from all its rows
+  const int wave_last_qi = min(Mb - 1, (row_ws + wave * 32 + 31) / grp);
   const int qi = row / grp;                       // chunk token of the row
   const int hq = h * grp + row % grp;
   const bool active = qi < Mb;
@@ -239,8 +271,19 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
   };
   // the registers of tile k into LDS: K as [token][d], V transposed [d][token]; entries past the
   // tile's keys are written as zeros
-  auto store = [&](int k) {
+  // (values as fp16 when the tag is true, with the wave's window flag for buffer par)
+  auto store = [&](int k, int par, auto as_f16) {
+    constexpr bool AS = decltype(as_f16)::value;
     const Tile tl = tile_of(k);
+    uint32_t mx = 0u, mn1 = 0xffffffffu;
+    auto vconv = [&](uint32_t w) -> uint32_t {
+      if constexpr (AS) {
+        mag_stats(mx, mn1, w);
+        return bf16x2_to_f16x2(w);
+      } else {
+        return w;
+      }
+    };
     if (tl.seg == 1) {
 #pragma unroll
       for (int m = 0; m < QITEMS; ++m) {
@@ -254,7 +297,7 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
           uint32_t* kd = reinterpret_cast<uint32_t*>(ks + t * KROW + g * C);
 #pragma unroll
           for (int e = 0; e < C / 2; ++e) {
-            const uint32_t vw = fv[(m * 4 + r) * (C / 2) + e] & keep;
+            const uint32_t vw = vconv(fv[(m * 4 + r) * (C / 2) + e] & keep);
             kd[e] = fk[(m * 4 + r) * (C / 2) + e] & keep;
             vt[(g * C + 2 * e) * kVRow + t] = (uint16_t)(vw & 0xffffu);
             vt[(g * C + 2 * e + 1) * kVRow + t] = (uint16_t)(vw >> 16);
@@ -271,11 +314,17 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
             u32x4{fk[4 * m] & keep, fk[4 * m + 1] & keep, fk[4 * m + 2] & keep, fk[4 * m + 3] & keep};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const uint32_t vw = fv[4 * m + w] & keep;
+          const uint32_t vw = vconv(fv[4 * m + w] & keep);
           vt[(8 * pc + 2 * w) * kVRow + t] = (uint16_t)(vw & 0xffffu);
           vt[(8 * pc + 2 * w + 1) * kVRow + t] = (uint16_t)(vw >> 16);
         }
       }
+    }
+    if constexpr (AS) {
+      const uint32_t top = max(mx >> 16, mx & 0xffffu), bot = min(mn1 >> 16, mn1 & 0xffffu);
+      const bool out = top >= kF16Hi || bot < kF16Lo - 1u;
+      const bool bad = __builtin_amdgcn_ballot_w64(out) != 0;
+      if (lane == 0) vbad[par][wave] = bad ? 1u : 0u;
     }
   };
 
@@ -285,7 +334,7 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
   // The softmax reference m_ref (log2 units) moves only when a score exceeds it by more than
   // 8: exponentials stay <= 2^8 and o, l are rescaled rarely.
   const float cl2 = p.scale_log2;
-  auto consume = [&](int count, int chunk_j0) {
+  auto consume = [&](int count, int chunk_j0, auto f16) {
     f32x16 s[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -343,22 +392,13 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
         psum += e;
       }
     l_run += psum;
-    // O^T += V^T P^T over 4 k-steps of 16 keys; P = hi + lo with hi the truncated upper half and
-    // lo = P - hi (exact) rounded to bf16 by the hardware conversion: 2^-16 relative
+    // O^T += V^T P^T over 4 k-steps of 16 keys.  fp16 tiles: P rounded to nearest fp16 (2^-11
+    // relative, 2^-25 absolute below 2^-14), one product.  bf16 tiles: P = hi + lo with hi the
+    // truncated upper half and lo = P - hi (exact) rounded to bf16 by the hardware conversion,
+    // 2^-16 relative, two products.
 #pragma unroll
     for (int kst = 0; kst < kKT / 16; ++kst) {
       const int mb = kst >> 1, r0 = 8 * (kst & 1);
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t ua = __float_as_uint(s[mb][r0 + 2 * j]), ub = __float_as_uint(s[mb][r0 + 2 * j + 1]);
-        hw[j] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
-        const f32x2 lo = {__uint_as_float(ua) - __uint_as_float(ua & 0xffff0000u),
-                          __uint_as_float(ub) - __uint_as_float(ub & 0xffff0000u)};
-        lw[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
-      }
-      const u32x4 bh = {hw[0], hw[1], hw[2], hw[3]};
-      const u32x4 bl = {lw[0], lw[1], lw[2], lw[3]};
       u32x4 a[DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -367,12 +407,42 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
         const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 8);
         a[db] = u32x4{v0.x, v0.y, v1.x, v1.y};
       }
+      if constexpr (decltype(f16)::value) {
+        uint32_t pw[4];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[db]), as_bf16x8(bh), o[db], 0, 0, 0);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[db]), as_bf16x8(bl), o[db], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) pw[j] = f16x2_rne(s[mb][r0 + 2 * j], s[mb][r0 + 2 * j + 1]);
+        const u32x4 bp = {pw[0], pw[1], pw[2], pw[3]};
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(a[db]), as_f16x8(bp), o[db], 0, 0, 0);
+      } else {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t ua = __float_as_uint(s[mb][r0 + 2 * j]), ub = __float_as_uint(s[mb][r0 + 2 * j + 1]);
+          hw[j] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
+          const f32x2 lo = {__uint_as_float(ua) - __uint_as_float(ua & 0xffff0000u),
+                            __uint_as_float(ub) - __uint_as_float(ub & 0xffff0000u)};
+          lw[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+        }
+        const u32x4 bh = {hw[0], hw[1], hw[2], hw[3]};
+        const u32x4 bl = {lw[0], lw[1], lw[2], lw[3]};
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[db]), as_bf16x8(bh), o[db], 0, 0, 0);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[db]), as_bf16x8(bl), o[db], 0, 0, 0);
+        }
       }
     }
+  };
+
+  // whether every value of the tile in buffer par lies in the fp16 window, from the waves'
+  // flags (read after the barrier that closes its staging)
+  auto tile_f16 = [&](int par) -> bool {
+    uint32_t f = 0u;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) f |= vbad[par][w];
+    return f == 0u;
   };
 
   // ---- the key tiles ------------------------------------------------------------------------------
@@ -386,45 +456,60 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
       __syncthreads();
     }
   }
-  fetch_idx(0, ik_n, iv_n, ok_n);
+  using f16_tag = std::integral_constant<bool, true>;
+  using bf16_tag = std::integral_constant<bool, false>;
   if constexpr (DBUF) {
-    // tile k + 1's keys and values load while tile k is consumed
-    // two LDS buffers: tile k + 1 is stored, and tile k + 2 loaded into registers, while tile k
-    // is consumed; one barrier per tile
-    fetch(0, ik_n, iv_n, ok_n);
-    if (1 < n_tiles) fetch_idx(1, ik_n, iv_n, ok_n);
-    store(0);
-    if (1 < n_tiles) {
-      fetch(1, ik_n, iv_n, ok_n);
-      if (2 < n_tiles) fetch_idx(2, ik_n, iv_n, ok_n);
-    }
-    for (int k = 0; k < n_tiles; ++k) {
-      __syncthreads();                // tile k is staged; every wave is done with tile k - 1
-      ks = ks2[k & 1];
-      vt = vt2[k & 1];
-      const Tile tl = tile_of(k);
-      consume(tl.count, tl.seg == 3 ? tl.start : -1);
-      // tile k + 1 is staged after the products of tile k are issued, so the staging work runs
-      // while they drain (its buffer last served tile k - 1, which the barrier above closed)
-      if (k + 1 < n_tiles) {
-        ks = ks2[(k + 1) & 1];
-        vt = vt2[(k + 1) & 1];
-        store(k + 1);
-        if (k + 2 < n_tiles) {
-          fetch(k + 2, ik_n, iv_n, ok_n);
-          if (k + 3 < n_tiles) fetch_idx(k + 3, ik_n, iv_n, ok_n);
+    // Two LDS buffers: tile k + 1 is stored, and tile k + 2 loaded into registers, while tile k
+    // is consumed; one barrier per tile.  Tiles k0, k0 + 1, ... in the tag's value format; the
+    // fp16 loop stops at a tile outside the fp16 window and returns its index (n_tiles at the end).
+    auto run = [&](int k0, auto tag) -> int {
+      constexpr bool AS = decltype(tag)::value;
+      fetch_idx(k0, ik_n, iv_n, ok_n);
+      fetch(k0, ik_n, iv_n, ok_n);
+      if (k0 + 1 < n_tiles) fetch_idx(k0 + 1, ik_n, iv_n, ok_n);
+      ks = ks2[k0 & 1];
+      vt = vt2[k0 & 1];
+      store(k0, k0 & 1, tag);
+      if (k0 + 1 < n_tiles) {
+        fetch(k0 + 1, ik_n, iv_n, ok_n);
+        if (k0 + 2 < n_tiles) fetch_idx(k0 + 2, ik_n, iv_n, ok_n);
+      }
+      for (int k = k0; k < n_tiles; ++k) {
+        __syncthreads();              // tile k is staged; every wave is done with tile k - 1
+        if constexpr (AS) {
+          if (!tile_f16(k & 1)) return k;   // (uniform) nobody reads tile k's buffers any more
+        }
+        ks = ks2[k & 1];
+        vt = vt2[k & 1];
+        const Tile tl = tile_of(k);
+        if (tl.seg != 3 || tl.start <= wave_last_qi) consume(tl.count, tl.seg == 3 ? tl.start : -1, tag);
+        // tile k + 1 is staged after the products of tile k are issued, so the staging work runs
+        // while they drain (its buffer last served tile k - 1, which the barrier above closed)
+        if (k + 1 < n_tiles) {
+          ks = ks2[(k + 1) & 1];
+          vt = vt2[(k + 1) & 1];
+          store(k + 1, (k + 1) & 1, tag);
+          if (k + 2 < n_tiles) {
+            fetch(k + 2, ik_n, iv_n, ok_n);
+            if (k + 3 < n_tiles) fetch_idx(k + 3, ik_n, iv_n, ok_n);
+          }
         }
       }
-    }
+      return n_tiles;
+    };
+    int k0 = 0;
+    if constexpr (F16) k0 = n_tiles > 0 ? run(0, f16_tag{}) : 0;
+    if (k0 < n_tiles) run(k0, bf16_tag{});
   } else {
+    fetch_idx(0, ik_n, iv_n, ok_n);
     for (int k = 0; k < n_tiles; ++k) {
       fetch(k, ik_n, iv_n, ok_n);
       if (k + 1 < n_tiles) fetch_idx(k + 1, ik_n, iv_n, ok_n);
       __syncthreads();                // every wave is done with the previous tile
-      store(k);
+      store(k, 0, bf16_tag{});
       __syncthreads();
       const Tile tl = tile_of(k);
-      consume(tl.count, tl.seg == 3 ? tl.start : -1);
+      if (tl.seg != 3 || tl.start <= wave_last_qi) consume(tl.count, tl.seg == 3 ? tl.start : -1, bf16_tag{});
     }
   }
 

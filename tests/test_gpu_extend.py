@@ -36,14 +36,11 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_extend_matches_oracle(name):
+def _run_extend(name, mutate=None, abs_scale=1.0):
+    """One extend launch of CASES[name] checked row by row against the oracle; mutate(case, kn, vn)
+    may change the host values before they are uploaded."""
     wl, layer, loop, lens, M, clens = CASES[name]
     case = H.Case(wl, layer, loop, lens, seed=4)
-    enc = case.oracle_encode()
-    idx_of = lambda kind, b, h: enc[kind, b, h][0]   # noqa: E731
-    case.gpu_setup()
-    case.d_pool.copy_(torch.from_numpy(case.oracle_pool(idx_of).reshape(-1)).to(H.DEV))
     B, Hq, Hkv, d = wl.batch, wl.q_heads, wl.kv_heads, wl.head_dim
     grp = Hq // Hkv
     kn = np.zeros((B, Hkv, M, d), np.uint16)
@@ -52,6 +49,12 @@ def test_extend_matches_oracle(name):
         for h in range(Hkv):
             kn[b, h] = gen.kv_tokens(wl, 0, layer, b, h, lens[b], lens[b] + M, loop, loop + 1, case.sc)[:, 0]
             vn[b, h] = gen.kv_tokens(wl, 1, layer, b, h, lens[b], lens[b] + M, loop, loop + 1, case.sc)[:, 0]
+    if mutate is not None:
+        mutate(case, kn, vn)
+    enc = case.oracle_encode()
+    idx_of = lambda kind, b, h: enc[kind, b, h][0]   # noqa: E731
+    case.gpu_setup()
+    case.d_pool.copy_(torch.from_numpy(case.oracle_pool(idx_of).reshape(-1)).to(H.DEV))
     q = gen.to_bf16_bits(np.random.default_rng(21).normal(size=(B, M, Hq, d)))
     out = torch.full((B, M, Hq, d), float("nan"), dtype=torch.float32, device=H.DEV)
     print(f"extend {name}: lens {lens}, chunk {M}", flush=True)
@@ -78,10 +81,56 @@ def test_extend_matches_oracle(name):
                 H.codebooks_f64(case.cbv, layer, case.jc, h), H.f64(case.kr[b, h, :n_rec]),
                 H.f64(case.vr[b, h, :n_rec]), H.f64(kn[b, h, :Mb]), H.f64(vn[b, h, :Mb]), case.tau, wl.chans, scale,
                 case.rot)
-            rel, mx = H.check_attention(got[b, :Mb, hq], o_ref)
+            # (abs_scale: the max-abs bound in units of the largest value magnitude, for values far from 1)
+            rel, mx = H.check_attention(got[b, :Mb, hq] / abs_scale, o_ref / abs_scale)
             worst = (max(worst[0], rel), max(worst[1], mx))
             checked += Mb
     print(f"  {checked} rows checked; worst rel-L2 {worst[0]:.2e}, max-abs {worst[1]:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_extend_matches_oracle(name):
+    _run_extend(name)
+
+
+def _scaled(bits, factor):
+    """bf16 bits times a power of two (exact for the normal values the generator makes)."""
+    return gen.to_bf16_bits(H.f64(bits) * factor)
+
+
+def _huge_recent(case, kn, vn):
+    # one value of 2^17 (beyond fp16) in the longest sequence's recent window: its workgroups switch
+    # to the bf16 value product after the prefix and vector-quantized tiles
+    b = int(np.argmax(case.lens))
+    assert case.split[b][2] > 5
+    case.vr[b, 0, 5, 3] = _scaled(np.array([0x3f80], np.uint16), 2.0 ** 17)[0]
+
+
+def _huge_chunk_tail(case, kn, vn):
+    # 2^16 (the first magnitude outside fp16) in the last chunk token of sequence 1
+    vn[1, 1, -1, 7] = _scaled(np.array([0x3f80], np.uint16), 2.0 ** 16)[0]
+
+
+def _tiny_values(case, kn, vn):
+    # every value (windows, chunk, the value rows of the cache and their codebooks) times 2^-20:
+    # below fp16's exact range, so every tile takes the bf16 product; the indices do not change
+    for arr in (case.vp, case.vr, vn):
+        arr[...] = _scaled(arr, 2.0 ** -20)
+    case.cbv = _scaled(case.cbv, 2.0 ** -20)
+    for key in list(case.kv):
+        if key[0] == 1:
+            case.kv[key] = _scaled(case.kv[key], 2.0 ** -20)
+
+
+@pytest.mark.parametrize("name,mode", [("d128", "huge_recent"), ("d128", "huge_chunk_tail"), ("d128", "tiny"),
+                                       ("c8_gqa", "tiny"), ("d64_gqa", "huge_recent")])
+def test_extend_values_outside_fp16(name, mode):
+    """Value tiles are multiplied in fp16 when all their values convert exactly; a tile with a value
+    of magnitude >= 2^16 (or non-finite) or a nonzero one below 2^-17 sends the rest of the
+    workgroup's tiles to the bf16 product.  Same tolerance as every extend case; for values of
+    2^17 the max-abs bound is taken relative to that magnitude."""
+    mut = {"huge_recent": _huge_recent, "huge_chunk_tail": _huge_chunk_tail, "tiny": _tiny_values}[mode]
+    _run_extend(name, mut, abs_scale=2.0 ** 17 if mode.startswith("huge") else 1.0)
 
 
 @pytest.mark.parametrize("c,G,d", [(4, 4, 128), (8, 2, 128), (4, 8, 64)])
