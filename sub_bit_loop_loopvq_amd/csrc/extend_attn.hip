@@ -38,6 +38,9 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kKT = 64;        // keys per tile
+// s_waitcnt immediate (gfx9 encoding): vector-memory count 0, the export and LDS/scalar counts
+// left at their maxima (no wait on them)
+constexpr int kWaitVmem0 = 0x0F70;
 constexpr int kVRow = kKT + 4; // bf16 per transposed V row (8 B of padding)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -206,26 +209,55 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
   uint32_t ik_n[QITEMS], iv_n[QITEMS];   // packed indices of the next tile
   bool ok_n[QITEMS];
 
-  // packed indices of a vector-quantized tile (token quads x group quads of one page: the tile
-  // is 64 aligned positions and a page holds a power of two >= 64, so one page per tile).  All
-  // loads are unconditional at clamped addresses; ok[] marks the real entries.
-  auto fetch_idx = [&](int k, uint32_t* ik, uint32_t* iv, bool* ok) {
-    const Tile tl = tile_of(k);
-    if (tl.seg != 1) return;
-    int page = p.block_table[(int64_t)b * p.max_pages + (tl.start >> p.pt_shift)];
+  // Packed indices of vector-quantized tiles.  Tile k's page id, then its index dwords, then its
+  // codewords are three dependent loads; each is requested a tile before the next needs it, and
+  // all three kinds are read at valid addresses for every tile ordinal (an ordinal outside the
+  // vector-quantized tiles reads a clamped one, marked not ok), so every tile issues the same
+  // loads.  Loads complete in issue order: a tile's waits all come before its new requests, so
+  // that a wait never covers a load issued in the same tile step.
+  const bool has_vq = t_vq > 0;    // (uniform) pool and block table are read only then
+  auto vq_tile = [&](int k) -> Tile {
+    const int j = min(max(k - t_pre, 0), t_vq - 1);
+    return {1, j * kKT, n_vq - j * kKT};
+  };
+  // the page of tile k (the tile is 64 aligned positions and a page holds a power of two >= 64, so
+  // one page per tile).  The offset carries a zero the compiler cannot see as uniform, so the id
+  // stays in a vector register until it is used instead of being moved to a scalar register, and
+  // waited for, at once.
+  auto fetch_page = [&](int k) -> int {
+    int vz;
+    asm("v_mov_b32 %0, 0" : "=v"(vz));
+    return p.block_table[(int64_t)b * p.max_pages + (vq_tile(k).start >> p.pt_shift) + vz];
+  };
+  // addresses of tile k's index dwords in its page (token quads x group quads), with ok flags
+  struct IdxPlan {
+    const uint8_t* at[QITEMS];
+    bool ok[QITEMS];
+  };
+  auto plan_idx = [&](int k, int page) -> IdxPlan {
+    const bool real = k < n_tiles && tile_of(k).seg == 1;
+    const Tile tl = vq_tile(k);
     const bool pok = page >= 0 && page < p.num_pages;
     page = pok ? page : 0;
+    IdxPlan ip;
 #pragma unroll
     for (int m = 0; m < QITEMS; ++m) {
       const int it0 = tid + NTH * m;
       const bool live = kAllLive || it0 < QIT;
       const int it = live ? it0 : 0;
       const int t = it % kKT, gq = it / kKT;
-      ok[m] = live && pok && t < tl.count;
+      ip.ok[m] = real && live && pok && t < tl.count;
       const int w = (tl.start + min(t, tl.count - 1)) & pt_mask;
-      const uint8_t* tile = pool_h + (int64_t)page * p.page_bytes + (((w >> 2) * (NG / 4) + gq) * 16 + (w & 3) * 4);
-      ik[m] = *reinterpret_cast<const uint32_t*>(tile);
-      iv[m] = *reinterpret_cast<const uint32_t*>(tile + p.kind_bytes);
+      ip.at[m] = pool_h + (int64_t)page * p.page_bytes + (((w >> 2) * (NG / 4) + gq) * 16 + (w & 3) * 4);
+    }
+    return ip;
+  };
+  auto issue_idx = [&](const IdxPlan& ip, uint32_t* ik, uint32_t* iv, bool* ok) {
+#pragma unroll
+    for (int m = 0; m < QITEMS; ++m) {
+      ik[m] = *reinterpret_cast<const uint32_t*>(ip.at[m]);
+      iv[m] = *reinterpret_cast<const uint32_t*>(ip.at[m] + p.kind_bytes);
+      ok[m] = ip.ok[m];
     }
   };
   bool ok_cur[QITEMS];   // ok flags of the tile whose keys are in fk / fv
@@ -456,6 +488,11 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
       __syncthreads();
     }
   }
+  // The q operand's loads are complete here on every path (the codebook staging above already
+  // waited for them when it ran).  Said explicitly, so the memory-counter waits inside the tile
+  // loop only cover the loop's own loads: otherwise the score products of every tile wait for all
+  // loads in flight, the next tiles' gathers included.
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
   using f16_tag = std::integral_constant<bool, true>;
   using bf16_tag = std::integral_constant<bool, false>;
   if constexpr (DBUF) {
@@ -464,15 +501,30 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
     // fp16 loop stops at a tile outside the fp16 window and returns its index (n_tiles at the end).
     auto run = [&](int k0, auto tag) -> int {
       constexpr bool AS = decltype(tag)::value;
-      fetch_idx(k0, ik_n, iv_n, ok_n);
+      const int last = n_tiles - 1;
+      // state entering tile k: tile k in LDS, tile k + 1's keys / values requested into fk / fv,
+      // tile k + 2's index dwords into ik_n / iv_n, tile k + 3's page id into pg_n
+      int pg_n = 0;
+      IdxPlan ip;
+      if (has_vq) {
+        issue_idx(plan_idx(k0, fetch_page(k0)), ik_n, iv_n, ok_n);
+        pg_n = fetch_page(min(k0 + 1, last));
+      }
       fetch(k0, ik_n, iv_n, ok_n);
-      if (k0 + 1 < n_tiles) fetch_idx(k0 + 1, ik_n, iv_n, ok_n);
+      if (has_vq) {
+        issue_idx(plan_idx(k0 + 1, pg_n), ik_n, iv_n, ok_n);
+        pg_n = fetch_page(min(k0 + 2, last));
+      }
       ks = ks2[k0 & 1];
       vt = vt2[k0 & 1];
       store(k0, k0 & 1, tag);
       if (k0 + 1 < n_tiles) {
+        if (has_vq) ip = plan_idx(k0 + 2, pg_n);
         fetch(k0 + 1, ik_n, iv_n, ok_n);
-        if (k0 + 2 < n_tiles) fetch_idx(k0 + 2, ik_n, iv_n, ok_n);
+        if (has_vq) {
+          issue_idx(ip, ik_n, iv_n, ok_n);
+          pg_n = fetch_page(min(k0 + 3, last));
+        }
       }
       for (int k = k0; k < n_tiles; ++k) {
         __syncthreads();              // tile k is staged; every wave is done with tile k - 1
@@ -490,8 +542,13 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
           vt = vt2[(k + 1) & 1];
           store(k + 1, (k + 1) & 1, tag);
           if (k + 2 < n_tiles) {
+            if (has_vq) ip = plan_idx(k + 3, pg_n);
+            __builtin_amdgcn_sched_barrier(0);
             fetch(k + 2, ik_n, iv_n, ok_n);
-            if (k + 3 < n_tiles) fetch_idx(k + 3, ik_n, iv_n, ok_n);
+            if (has_vq) {
+              issue_idx(ip, ik_n, iv_n, ok_n);
+              pg_n = fetch_page(min(k + 4, last));
+            }
           }
         }
       }
@@ -501,10 +558,10 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
     if constexpr (F16) k0 = n_tiles > 0 ? run(0, f16_tag{}) : 0;
     if (k0 < n_tiles) run(k0, bf16_tag{});
   } else {
-    fetch_idx(0, ik_n, iv_n, ok_n);
+    if (has_vq) issue_idx(plan_idx(0, fetch_page(0)), ik_n, iv_n, ok_n);
     for (int k = 0; k < n_tiles; ++k) {
       fetch(k, ik_n, iv_n, ok_n);
-      if (k + 1 < n_tiles) fetch_idx(k + 1, ik_n, iv_n, ok_n);
+      if (has_vq && k + 1 < n_tiles) issue_idx(plan_idx(k + 1, fetch_page(k + 1)), ik_n, iv_n, ok_n);
       __syncthreads();                // every wave is done with the previous tile
       store(k, 0, bf16_tag{});
       __syncthreads();
