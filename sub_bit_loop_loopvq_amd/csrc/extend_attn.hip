@@ -102,6 +102,7 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
   constexpr bool F16 = !ROT;
   constexpr int NWAVE = NTH / 64;
   __shared__ uint32_t vbad[2][NWAVE];   // per buffer and wave: a value outside the fp16 window
+  __shared__ uint32_t vslice_bad[NWAVE];   // per wave: a value of the value codebook slice outside it
   uint16_t* ks = ks2[0];
   uint16_t* vt = vt2[0];
 
@@ -308,9 +309,10 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
     constexpr bool AS = decltype(as_f16)::value;
     const Tile tl = tile_of(k);
     uint32_t mx = 0u, mn1 = 0xffffffffu;
-    auto vconv = [&](uint32_t w) -> uint32_t {
+    // (vector-quantized values come from the codebook slice, checked once per workgroup)
+    auto vconv = [&](uint32_t w, auto chk) -> uint32_t {
       if constexpr (AS) {
-        mag_stats(mx, mn1, w);
+        if constexpr (decltype(chk)::value) mag_stats(mx, mn1, w);
         return bf16x2_to_f16x2(w);
       } else {
         return w;
@@ -329,7 +331,7 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
           uint32_t* kd = reinterpret_cast<uint32_t*>(ks + t * KROW + g * C);
 #pragma unroll
           for (int e = 0; e < C / 2; ++e) {
-            const uint32_t vw = vconv(fv[(m * 4 + r) * (C / 2) + e] & keep);
+            const uint32_t vw = vconv(fv[(m * 4 + r) * (C / 2) + e] & keep, std::false_type{});
             kd[e] = fk[(m * 4 + r) * (C / 2) + e] & keep;
             vt[(g * C + 2 * e) * kVRow + t] = (uint16_t)(vw & 0xffffu);
             vt[(g * C + 2 * e + 1) * kVRow + t] = (uint16_t)(vw >> 16);
@@ -346,7 +348,7 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
             u32x4{fk[4 * m] & keep, fk[4 * m + 1] & keep, fk[4 * m + 2] & keep, fk[4 * m + 3] & keep};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const uint32_t vw = vconv(fv[4 * m + w] & keep);
+          const uint32_t vw = vconv(fv[4 * m + w] & keep, std::true_type{});
           vt[(8 * pc + 2 * w) * kVRow + t] = (uint16_t)(vw & 0xffffu);
           vt[(8 * pc + 2 * w + 1) * kVRow + t] = (uint16_t)(vw >> 16);
         }
@@ -414,6 +416,8 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
     }
     // (a row with nothing visible yet keeps m_ref = -inf and uses 0, so exp2(-inf) = 0)
     const float nm = m_ref == -INFINITY ? 0.f : -m_ref;
+    // l: the sum of the weights the value product uses (fp16 tiles: of the rounded ones, added
+    // pairwise by v_dot2_f32_f16 while they are packed)
     float psum = 0.f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -421,9 +425,8 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
       for (int r = 0; r < 16; ++r) {
         const float e = __builtin_amdgcn_exp2f(fmaf(s[mb][r], cl2, nm));
         s[mb][r] = e;
-        psum += e;
+        if constexpr (!decltype(f16)::value) psum += e;
       }
-    l_run += psum;
     // O^T += V^T P^T over 4 k-steps of 16 keys.  fp16 tiles: P rounded to nearest fp16 (2^-11
     // relative, 2^-25 absolute below 2^-14), one product.  bf16 tiles: P = hi + lo with hi the
     // truncated upper half and lo = P - hi (exact) rounded to bf16 by the hardware conversion,
@@ -442,7 +445,10 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
       if constexpr (decltype(f16)::value) {
         uint32_t pw[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pw[j] = f16x2_rne(s[mb][r0 + 2 * j], s[mb][r0 + 2 * j + 1]);
+        for (int j = 0; j < 4; ++j) {
+          pw[j] = f16x2_rne(s[mb][r0 + 2 * j], s[mb][r0 + 2 * j + 1]);
+          psum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pw[j]), f16x2{1.0f16, 1.0f16}, psum, false);
+        }
         const u32x4 bp = {pw[0], pw[1], pw[2], pw[3]};
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -466,6 +472,7 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
         }
       }
     }
+    l_run += psum;
   };
 
   // whether every value of the tile in buffer par lies in the fp16 window, from the waves'
@@ -478,6 +485,7 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
   };
 
   // ---- the key tiles ------------------------------------------------------------------------------
+  bool vq_f16 = true;   // every value of the value codebook slice lies in the fp16 window
   if constexpr (CBL) {
     if (t_vq > 0) {   // (uniform) the key codebook slice into LDS, 16 B per thread and step
       constexpr int PER = kCodes * D * 2 / 16 / NTH;
@@ -485,7 +493,25 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
 #pragma unroll
       for (int m = 0; m < PER; ++m)
         reinterpret_cast<u32x4*>(cbk_l)[tid + NTH * m] = reinterpret_cast<const u32x4*>(slice_k)[tid + NTH * m];
+      if constexpr (F16) {   // the value slice against the fp16 window, once
+        uint32_t mx = 0u, mn1 = 0xffffffffu;
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+          const u32x4 w = reinterpret_cast<const u32x4*>(slice_v)[tid + NTH * m];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mag_stats(mx, mn1, w[e]);
+        }
+        const uint32_t top = max(mx >> 16, mx & 0xffffu), bot = min(mn1 >> 16, mn1 & 0xffffu);
+        const bool bad = __builtin_amdgcn_ballot_w64(top >= kF16Hi || bot < kF16Lo - 1u) != 0;
+        if (lane == 0) vslice_bad[wave] = bad ? 1u : 0u;
+      }
       __syncthreads();
+      if constexpr (F16) {
+        uint32_t f = 0u;
+#pragma unroll
+        for (int w = 0; w < NWAVE; ++w) f |= vslice_bad[w];
+        vq_f16 = f == 0u;
+      }
     }
   }
   // The q operand's loads are complete here on every path (the codebook staging above already
@@ -555,7 +581,7 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
       return n_tiles;
     };
     int k0 = 0;
-    if constexpr (F16) k0 = n_tiles > 0 ? run(0, f16_tag{}) : 0;
+    if constexpr (F16) k0 = n_tiles > 0 && vq_f16 ? run(0, f16_tag{}) : 0;
     if (k0 < n_tiles) run(k0, bf16_tag{});
   } else {
     if (has_vq) issue_idx(plan_idx(0, fetch_page(0)), ik_n, iv_n, ok_n);

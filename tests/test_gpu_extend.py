@@ -122,14 +122,25 @@ def _tiny_values(case, kn, vn):
             case.kv[key] = _scaled(case.kv[key], 2.0 ** -20)
 
 
+def _huge_codebook(case, kn, vn):
+    # the vector-quantized values (the value codebooks and the rows they encode) times 2^16: the
+    # codebook slice fails the per-workgroup check, and every tile takes the bf16 product
+    case.cbv = _scaled(case.cbv, 2.0 ** 16)
+    for key in list(case.kv):
+        if key[0] == 1:
+            case.kv[key] = _scaled(case.kv[key], 2.0 ** 16)
+
+
 @pytest.mark.parametrize("name,mode", [("d128", "huge_recent"), ("d128", "huge_chunk_tail"), ("d128", "tiny"),
-                                       ("c8_gqa", "tiny"), ("d64_gqa", "huge_recent")])
+                                       ("c8_gqa", "tiny"), ("d64_gqa", "huge_recent"), ("d128", "huge_codebook")])
 def test_extend_values_outside_fp16(name, mode):
     """Value tiles are multiplied in fp16 when all their values convert exactly; a tile with a value
     of magnitude >= 2^16 (or non-finite) or a nonzero one below 2^-17 sends the rest of the
-    workgroup's tiles to the bf16 product.  Same tolerance as every extend case; for values of
+    workgroup's tiles to the bf16 product, and so does such a value anywhere in the kv-head's value
+    codebook slice (checked once, before the first tile).  Same tolerance as every extend case; for values of
     2^17 the max-abs bound is taken relative to that magnitude."""
-    mut = {"huge_recent": _huge_recent, "huge_chunk_tail": _huge_chunk_tail, "tiny": _tiny_values}[mode]
+    mut = {"huge_recent": _huge_recent, "huge_chunk_tail": _huge_chunk_tail, "tiny": _tiny_values,
+           "huge_codebook": _huge_codebook}[mode]
     _run_extend(name, mut, abs_scale=2.0 ** 17 if mode.startswith("huge") else 1.0)
 
 
