@@ -33,6 +33,9 @@ CASES = {
     # c=4 over G=8 loop steps (0.25 bit), loop step 6 of its group
     "c4_g8": (W.LAYER_4K.with_(loops=8, loop_group=8, batch=2, q_heads=4, kv_heads=2, context=400), 0, 6, [300, 90],
               50, None),
+    # d=128 with 256-token pages: four 64-token key tiles per page, the last page partly used
+    "d128_page256": (W.LAYER_4K.with_(batch=2, q_heads=4, kv_heads=2, context=900, page_tokens=256), 0, 1, [900, 333],
+                     100, [100, 37]),
 }
 
 

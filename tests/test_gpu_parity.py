@@ -129,6 +129,13 @@ def test_d64_page128_chain():
     _chain(H.Case(wl, 0, 3, [800, 200, 450], seed=5), decode_splits=(0, 4))
 
 
+def test_d128_page256_chain():
+    """d=128 (32 channel groups) with 256-token pages: eight 32-token decode tiles per page."""
+    wl = W.LAYER_4K.with_(batch=3, q_heads=2, kv_heads=2, context=1100, page_tokens=256)
+    _say("d128 page256 chain")
+    _chain(H.Case(wl, 0, 2, [1100, 300, 713], seed=8), decode_splits=(0, 3))
+
+
 def test_large_scores_take_exact_maximum_path():
     """Scores far above the first tile's maximum (scale 50x) force the split's exact-maximum redo."""
     wl = SMALL.with_(batch=2, q_heads=2, kv_heads=2, context=1500)
