@@ -99,7 +99,7 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
   // Without a rotation the value tiles are staged as fp16 and the value product runs on fp16
   // MFMAs with P rounded to fp16: one product instead of the bf16 hi + lo pair.  The first tile
   // with a value outside the fp16 window ends that loop; a second loop, in bf16, goes on from it.
-  constexpr bool F16 = !ROT;
+  constexpr bool F16 = true;
   constexpr int NWAVE = NTH / 64;
   __shared__ uint32_t vbad[2][NWAVE];   // per buffer and wave: a value outside the fp16 window
   __shared__ uint32_t vslice_bad[NWAVE];   // per wave: a value of the value codebook slice outside it
@@ -486,33 +486,30 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
 
   // ---- the key tiles ------------------------------------------------------------------------------
   bool vq_f16 = true;   // every value of the value codebook slice lies in the fp16 window
-  if constexpr (CBL) {
-    if (t_vq > 0) {   // (uniform) the key codebook slice into LDS, 16 B per thread and step
-      constexpr int PER = kCodes * D * 2 / 16 / NTH;
-      static_assert(PER * NTH * 16 == kCodes * D * 2, "codebook staging");
+  if (t_vq > 0) {   // (uniform)
+    constexpr int PER = kCodes * D * 2 / 16 / NTH;
+    static_assert(PER * NTH * 16 == kCodes * D * 2, "codebook staging");
+    if constexpr (CBL) {   // the key codebook slice into LDS, 16 B per thread and step
 #pragma unroll
       for (int m = 0; m < PER; ++m)
         reinterpret_cast<u32x4*>(cbk_l)[tid + NTH * m] = reinterpret_cast<const u32x4*>(slice_k)[tid + NTH * m];
-      if constexpr (F16) {   // the value slice against the fp16 window, once
-        uint32_t mx = 0u, mn1 = 0xffffffffu;
-#pragma unroll
-        for (int m = 0; m < PER; ++m) {
-          const u32x4 w = reinterpret_cast<const u32x4*>(slice_v)[tid + NTH * m];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) mag_stats(mx, mn1, w[e]);
-        }
-        const uint32_t top = max(mx >> 16, mx & 0xffffu), bot = min(mn1 >> 16, mn1 & 0xffffu);
-        const bool bad = __builtin_amdgcn_ballot_w64(top >= kF16Hi || bot < kF16Lo - 1u) != 0;
-        if (lane == 0) vslice_bad[wave] = bad ? 1u : 0u;
-      }
-      __syncthreads();
-      if constexpr (F16) {
-        uint32_t f = 0u;
-#pragma unroll
-        for (int w = 0; w < NWAVE; ++w) f |= vslice_bad[w];
-        vq_f16 = f == 0u;
-      }
     }
+    // the value slice against the fp16 window, once
+    uint32_t mx = 0u, mn1 = 0xffffffffu;
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const u32x4 w = reinterpret_cast<const u32x4*>(slice_v)[tid + NTH * m];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mag_stats(mx, mn1, w[e]);
+    }
+    const uint32_t top = max(mx >> 16, mx & 0xffffu), bot = min(mn1 >> 16, mn1 & 0xffffu);
+    const bool bad = __builtin_amdgcn_ballot_w64(top >= kF16Hi || bot < kF16Lo - 1u) != 0;
+    if (lane == 0) vslice_bad[wave] = bad ? 1u : 0u;
+    __syncthreads();
+    uint32_t f = 0u;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) f |= vslice_bad[w];
+    vq_f16 = f == 0u;
   }
   // The q operand's loads are complete here on every path (the codebook staging above already
   // waited for them when it ran).  Said explicitly, so the memory-counter waits inside the tile
@@ -584,16 +581,28 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
     if constexpr (F16) k0 = n_tiles > 0 && vq_f16 ? run(0, f16_tag{}) : 0;
     if (k0 < n_tiles) run(k0, bf16_tag{});
   } else {
-    if (has_vq) issue_idx(plan_idx(0, fetch_page(0)), ik_n, iv_n, ok_n);
-    for (int k = 0; k < n_tiles; ++k) {
-      fetch(k, ik_n, iv_n, ok_n);
-      if (has_vq && k + 1 < n_tiles) issue_idx(plan_idx(k + 1, fetch_page(k + 1)), ik_n, iv_n, ok_n);
-      __syncthreads();                // every wave is done with the previous tile
-      store(k, 0, bf16_tag{});
-      __syncthreads();
-      const Tile tl = tile_of(k);
-      if (tl.seg != 3 || tl.start <= wave_last_qi) consume(tl.count, tl.seg == 3 ? tl.start : -1, bf16_tag{});
-    }
+    // one LDS buffer: tile k is fetched, stored between two barriers and consumed (the fp16 loop
+    // stops at a tile outside the fp16 window, as above)
+    auto run1 = [&](int k0, auto tag) -> int {
+      constexpr bool AS = decltype(tag)::value;
+      if (has_vq) issue_idx(plan_idx(k0, fetch_page(k0)), ik_n, iv_n, ok_n);
+      for (int k = k0; k < n_tiles; ++k) {
+        fetch(k, ik_n, iv_n, ok_n);
+        if (has_vq && k + 1 < n_tiles) issue_idx(plan_idx(k + 1, fetch_page(k + 1)), ik_n, iv_n, ok_n);
+        __syncthreads();              // every wave is done with the previous tile
+        store(k, 0, tag);
+        __syncthreads();
+        if constexpr (AS) {
+          if (!tile_f16(0)) return k;   // (uniform)
+        }
+        const Tile tl = tile_of(k);
+        if (tl.seg != 3 || tl.start <= wave_last_qi) consume(tl.count, tl.seg == 3 ? tl.start : -1, tag);
+      }
+      return n_tiles;
+    };
+    int k0 = 0;
+    if (vq_f16) k0 = run1(0, f16_tag{});
+    if (k0 < n_tiles) run1(k0, bf16_tag{});
   }
 
   // ---- normalise and write: O^T register r of block db is channel 32db + 8(r/4) + 4half + r%4

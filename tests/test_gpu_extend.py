@@ -135,7 +135,8 @@ def _huge_codebook(case, kn, vn):
 
 
 @pytest.mark.parametrize("name,mode", [("d128", "huge_recent"), ("d128", "huge_chunk_tail"), ("d128", "tiny"),
-                                       ("c8_gqa", "tiny"), ("d64_gqa", "huge_recent"), ("d128", "huge_codebook")])
+                                       ("c8_gqa", "tiny"), ("d64_gqa", "huge_recent"), ("d128", "huge_codebook"),
+                                       ("c8_rot", "huge_recent"), ("c8_rot", "huge_codebook")])
 def test_extend_values_outside_fp16(name, mode):
     """Value tiles are multiplied in fp16 when all their values convert exactly; a tile with a value
     of magnitude >= 2^16 (or non-finite) or a nonzero one below 2^-17 sends the rest of the
