@@ -9,21 +9,21 @@
 // loop-step-tau slice of codeword idx[n][g] of (layer, kv-head, group g).
 //
 // How (MI355X):
-//  * workgroup = 128 query rows (row = (chunk token, q-head of the kv-head)) of one
-//    (sequence, kv-head); 4 waves of 32 rows.  Keys come in tiles of 64 tokens.
-//  * each tile is staged in LDS by the whole workgroup: K as [token][d] bf16 rows and V
-//    transposed as [d][token] bf16 (rows padded so the MFMA operand reads hit distinct banks).
-//    Vector-quantized tokens are dequantized on the way: the packed index byte of (token,
-//    group) selects the c channels of that group's loop-step slice, read from the group-major
-//    codebook copy ([tau][g][k][i]), so a tile's gathers of one group stay within K x c
-//    elements (2 KB at c=4) and share cache lines.
+//  * workgroup = 256 query rows (row = (chunk token, q-head of the kv-head)) of one
+//    (sequence, kv-head); 8 waves of 32 rows, one workgroup per CU.  Keys come in tiles of 64
+//    tokens, staged in LDS by the whole workgroup into two buffers (tile k + 1 while tile k is
+//    consumed): K as [token][d] bf16 rows and V transposed as [d][token] (rows padded so the
+//    MFMA operand reads hit distinct banks).  Vector-quantized tokens are dequantized on the
+//    way: the packed index byte of (token, group) selects the c channels of that group's
+//    loop-step slice; keys from the kv-head's key slice, copied to LDS once, values from the
+//    group-major codebook copy ([tau][g][k][i]) in L2.
 //  * per wave: S^T = K Q^T on bf16 32x32x16 MFMAs (a rotated q' = R^T q is split into two
-//    bf16 parts, two MFMAs), online softmax in log2 units with the causal mask of the
-//    chunk, then O^T += V^T P^T with P split into two bf16 parts (hi + lo, 2^-16 relative),
-//    so the products keep fp32-level accuracy.  The D-layout of S^T (lane = query row,
-//    registers = tokens) is directly the B operand of the second product once its 16
-//    tokens are taken in the order the registers hold them; the V^T operand reads the same
-//    order.
+//    bf16 parts, two MFMAs), online softmax in log2 units with the causal mask of the chunk,
+//    then O^T += V^T P^T: on fp16 MFMAs with P rounded to fp16 while every value converts to
+//    fp16 exactly, else with P split into two bf16 parts (hi + lo, 2^-16 relative).  The
+//    D-layout of S^T (lane = query row, registers = tokens) is directly the B operand of the
+//    second product once its 16 tokens are taken in the order the registers hold them; the
+//    V^T operand reads the same order.
 #include "lvq_common.h"
 
 namespace lvq {
@@ -78,28 +78,24 @@ __device__ __forceinline__ void split2(float v, uint32_t& hi, uint32_t& lo) {
 }
 
 template <int NG, int C, bool ROT>
-__global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(ExtendParams p) {
-  // Without a rotation: 8 waves (256 query rows) per workgroup, one workgroup per CU, so each
-  // staged tile serves twice the rows; with one, 4 waves and two workgroups per CU.
-  constexpr int NTH = ROT ? 256 : 512;
+__global__ void __launch_bounds__(512, 1) extend_kernel(ExtendParams p) {
+  // 8 waves (256 query rows) per workgroup, one workgroup per CU, so that each staged tile
+  // serves 256 rows.
+  constexpr int NTH = 512;
   constexpr int kRows = NTH / 2;
   constexpr int D = NG * C;
   constexpr int KROW = D + 8;         // bf16 per K row (16 B of padding)
   constexpr int KSTEPS = D / 16;      // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;          // 32-channel blocks of O^T
-  // Without a rotation: two K / V^T tile buffers (tile k + 1 is staged while tile k is consumed)
-  // and the key codebook's loop-step slice of the kv-head in LDS (its K x d bf16, loaded once), so
-  // that the dequantization of vector-quantized keys gathers from LDS instead of L2; q stays in
-  // registers.
-  constexpr bool DBUF = !ROT;
-  constexpr bool CBL = !ROT;
-  __shared__ __align__(16) uint16_t ks2[DBUF ? 2 : 1][kKT * KROW];
-  __shared__ __align__(16) uint16_t vt2[DBUF ? 2 : 1][D * kVRow];
-  __shared__ __align__(16) uint16_t cbk_l[CBL ? kCodes * D : 8];
-  // Without a rotation the value tiles are staged as fp16 and the value product runs on fp16
-  // MFMAs with P rounded to fp16: one product instead of the bf16 hi + lo pair.  The first tile
-  // with a value outside the fp16 window ends that loop; a second loop, in bf16, goes on from it.
-  constexpr bool F16 = true;
+  // Two K / V^T tile buffers (tile k + 1 is staged while tile k is consumed) and the key
+  // codebook's loop-step slice of the kv-head in LDS (its K x d bf16, loaded once), so that the
+  // dequantization of vector-quantized keys gathers from LDS instead of L2; q stays in registers.
+  __shared__ __align__(16) uint16_t ks2[2][kKT * KROW];
+  __shared__ __align__(16) uint16_t vt2[2][D * kVRow];
+  __shared__ __align__(16) uint16_t cbk_l[kCodes * D];
+  // The value tiles are staged as fp16 and the value product runs on fp16 MFMAs with P rounded
+  // to fp16: one product instead of the bf16 hi + lo pair.  The first tile with a value outside
+  // the fp16 window ends that loop; a second loop, in bf16, goes on from it.
   constexpr int NWAVE = NTH / 64;
   __shared__ uint32_t vbad[2][NWAVE];   // per buffer and wave: a value outside the fp16 window
   __shared__ uint32_t vslice_bad[NWAVE];   // per wave: a value of the value codebook slice outside it
@@ -201,11 +197,14 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
 
   constexpr int PIECES = D / 8;                     // 16-byte pieces per bf16 row
   constexpr int RITEMS = kKT * PIECES / NTH;        // row pieces per thread
-  constexpr int QIT = kKT * (NG / 4);               // (token, group quad) items of a tile
+  // vector-quantized items: (token, GPI consecutive groups inside one group quad), as many as
+  // there are threads when the quads allow it (fewer staging registers per thread at c = 8)
+  constexpr int GPI = NG * kKT / NTH >= 4 ? 4 : (NG * kKT / NTH >= 2 ? 2 : 1);
+  constexpr int QIT = kKT * (NG / GPI);             // items of a tile
   constexpr int QITEMS = (QIT + NTH - 1) / NTH;     // per thread (the last may be idle)
   constexpr bool kAllLive = QIT % NTH == 0;
   static_assert(RITEMS >= 1 && RITEMS * NTH == kKT * PIECES && QITEMS >= 1, "tile mapping");
-  constexpr int FB = RITEMS * 4 > QITEMS * 4 * (C / 2) ? RITEMS * 4 : QITEMS * 4 * (C / 2);   // dwords per kind
+  constexpr int FB = RITEMS * 4 > QITEMS * GPI * (C / 2) ? RITEMS * 4 : QITEMS * GPI * (C / 2);   // dwords per kind
   uint32_t fk[FB], fv[FB];          // the tile's keys / values on their way to LDS
   uint32_t ik_n[QITEMS], iv_n[QITEMS];   // packed indices of the next tile
   bool ok_n[QITEMS];
@@ -246,7 +245,7 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
       const int it0 = tid + NTH * m;
       const bool live = kAllLive || it0 < QIT;
       const int it = live ? it0 : 0;
-      const int t = it % kKT, gq = it / kKT;
+      const int t = it % kKT, gq = (it / kKT) * GPI / 4;   // the item's group quad
       ip.ok[m] = real && live && pok && t < tl.count;
       const int w = (tl.start + min(t, tl.count - 1)) & pt_mask;
       ip.at[m] = pool_h + (int64_t)page * p.page_bytes + (((w >> 2) * (NG / 4) + gq) * 16 + (w & 3) * 4);
@@ -271,17 +270,17 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
       for (int m = 0; m < QITEMS; ++m) {
         ok_cur[m] = ok[m];
         const int it0 = tid + NTH * m;
-        const int gq = (kAllLive || it0 < QIT ? it0 : 0) / kKT;
+        const int g0 = GPI * ((kAllLive || it0 < QIT ? it0 : 0) / kKT);   // first group of the item
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int g = 4 * gq + r;
-          const uint32_t kx = (ik[m] >> (8 * r)) & 0xffu, vx = (iv[m] >> (8 * r)) & 0xffu;
-          const uint32_t* kc = reinterpret_cast<const uint32_t*>((CBL ? cbk_l : slice_k) + (g * kCodes + kx) * C);
+        for (int r = 0; r < GPI; ++r) {
+          const int g = g0 + r, sh = 8 * (g & 3);   // index byte g % 4 of the quad's dword
+          const uint32_t kx = (ik[m] >> sh) & 0xffu, vx = (iv[m] >> sh) & 0xffu;
+          const uint32_t* kc = reinterpret_cast<const uint32_t*>(cbk_l + (g * kCodes + kx) * C);
           const uint32_t* vc = reinterpret_cast<const uint32_t*>(slice_v + (g * kCodes + vx) * C);
 #pragma unroll
           for (int e = 0; e < C / 2; ++e) {
-            fk[(m * 4 + r) * (C / 2) + e] = kc[e];
-            fv[(m * 4 + r) * (C / 2) + e] = vc[e];
+            fk[(m * GPI + r) * (C / 2) + e] = kc[e];
+            fv[(m * GPI + r) * (C / 2) + e] = vc[e];
           }
         }
       }
@@ -323,16 +322,16 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
       for (int m = 0; m < QITEMS; ++m) {
         const int it = tid + NTH * m;
         if (!kAllLive && it >= QIT) continue;
-        const int t = it % kKT, gq = it / kKT;
+        const int t = it % kKT, g0 = GPI * (it / kKT);
         const uint32_t keep = ok_cur[m] ? 0xffffffffu : 0u;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int g = 4 * gq + r;
+        for (int r = 0; r < GPI; ++r) {
+          const int g = g0 + r;
           uint32_t* kd = reinterpret_cast<uint32_t*>(ks + t * KROW + g * C);
 #pragma unroll
           for (int e = 0; e < C / 2; ++e) {
-            const uint32_t vw = vconv(fv[(m * 4 + r) * (C / 2) + e] & keep, std::false_type{});
-            kd[e] = fk[(m * 4 + r) * (C / 2) + e] & keep;
+            const uint32_t vw = vconv(fv[(m * GPI + r) * (C / 2) + e] & keep, std::false_type{});
+            kd[e] = fk[(m * GPI + r) * (C / 2) + e] & keep;
             vt[(g * C + 2 * e) * kVRow + t] = (uint16_t)(vw & 0xffffu);
             vt[(g * C + 2 * e + 1) * kVRow + t] = (uint16_t)(vw >> 16);
           }
@@ -369,106 +368,124 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
   // 8: exponentials stay <= 2^8 and o, l are rescaled rarely.
   const float cl2 = p.scale_log2;
   auto consume = [&](int count, int chunk_j0, auto f16) {
-    f32x16 s[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      // all of the block's K operands first, so the LDS reads overlap instead of each MFMA
-      // waiting for its own
-      u32x4 a[KSTEPS];
-      const uint16_t* krow = ks + (32 * mb + col) * KROW + 8 * half;
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) a[kk] = *reinterpret_cast<const u32x4*>(krow + 16 * kk);
-      f32x16 acc = {};
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[kk]), as_bf16x8(bq[kk]), acc, 0, 0, 0);
-        if constexpr (ROT)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[kk]), as_bf16x8(bq_lo[kk]), acc, 0, 0, 0);
-      }
-      s[mb] = acc;
-    }
-    // raw scores; token of register r of block mb: 32mb + 8(r/4) + 4half + r%4
-    if (count < kKT || chunk_j0 >= 0) {   // (uniform) a tile with keys to hide
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = 32 * mb + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = t < count && (chunk_j0 < 0 || chunk_j0 + t <= qi);
-          s[mb][r] = vis ? s[mb][r] : -INFINITY;
-        }
-    }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[mb][r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * cl2;
-    const bool move = tmax > m_ref + 8.f;       // m_ref = -inf: any visible key moves it
-    if (__builtin_amdgcn_ballot_w64(move)) {
-      const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - tmax) : 1.f;   // m_ref = -inf -> 0
-      m_ref = move ? tmax : m_ref;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    }
-    // (a row with nothing visible yet keeps m_ref = -inf and uses 0, so exp2(-inf) = 0)
-    const float nm = m_ref == -INFINITY ? 0.f : -m_ref;
-    // l: the sum of the weights the value product uses (fp16 tiles: of the rounded ones, added
-    // pairwise by v_dot2_f32_f16 while they are packed)
+    // (with a rotation the lane's operand addresses are recomputed from a fresh lane id in every
+    // tile, so that they are not kept live, or spilled, across the tile loop)
+    int lane_f = lane;
+    if constexpr (ROT) asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_f));
+    const int col = lane_f & 31, half = lane_f >> 5;
+    // NB 32-key blocks per pass: without a rotation both blocks of the tile in one pass; with one
+    // (q' in two parts takes 32 more registers), one block per pass, so that the scores and the
+    // key operands of only half the tile are live at once.
+    constexpr int NB = ROT ? 1 : 2;
+    constexpr int KB = ROT ? KSTEPS / 2 : KSTEPS;   // key operands loaded together
     float psum = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int pass = 0; pass < 2 / NB; ++pass) {
+      f32x16 s[NB];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[mb][r], cl2, nm));
-        s[mb][r] = e;
-        if constexpr (!decltype(f16)::value) psum += e;
-      }
-    // O^T += V^T P^T over 4 k-steps of 16 keys.  fp16 tiles: P rounded to nearest fp16 (2^-11
-    // relative, 2^-25 absolute below 2^-14), one product.  bf16 tiles: P = hi + lo with hi the
-    // truncated upper half and lo = P - hi (exact) rounded to bf16 by the hardware conversion,
-    // 2^-16 relative, two products.
+      for (int b = 0; b < NB; ++b) {
+        const int mb = pass * NB + b;
+        const uint16_t* krow = ks + (32 * mb + col) * KROW + 8 * half;
+        f32x16 acc = {};
 #pragma unroll
-    for (int kst = 0; kst < kKT / 16; ++kst) {
-      const int mb = kst >> 1, r0 = 8 * (kst & 1);
-      u32x4 a[DB];
+        for (int k0 = 0; k0 < KSTEPS; k0 += KB) {
+          // KB of the block's K operands first, so the LDS reads overlap instead of each MFMA
+          // waiting for its own
+          u32x4 a[KB];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint16_t* vrow = vt + (32 * db + col) * kVRow + 16 * kst + 4 * half;
-        const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 8);
-        a[db] = u32x4{v0.x, v0.y, v1.x, v1.y};
-      }
-      if constexpr (decltype(f16)::value) {
-        uint32_t pw[4];
+          for (int kk = 0; kk < KB; ++kk) a[kk] = *reinterpret_cast<const u32x4*>(krow + 16 * (k0 + kk));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          pw[j] = f16x2_rne(s[mb][r0 + 2 * j], s[mb][r0 + 2 * j + 1]);
-          psum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pw[j]), f16x2{1.0f16, 1.0f16}, psum, false);
+          for (int kk = 0; kk < KB; ++kk) {
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[kk]), as_bf16x8(bq[k0 + kk]), acc, 0, 0, 0);
+            if constexpr (ROT)
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[kk]), as_bf16x8(bq_lo[k0 + kk]), acc, 0, 0, 0);
+          }
         }
-        const u32x4 bp = {pw[0], pw[1], pw[2], pw[3]};
+        s[b] = acc;
+      }
+      // raw scores; token of register r of block mb: 32mb + 8(r/4) + 4half + r%4
+      if (count < kKT || chunk_j0 >= 0) {   // (uniform) a tile with keys to hide
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int t = 32 * (pass * NB + b) + 8 * (r >> 2) + 4 * half + (r & 3);
+            const bool vis = t < count && (chunk_j0 < 0 || chunk_j0 + t <= qi);
+            s[b][r] = vis ? s[b][r] : -INFINITY;
+          }
+      }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[b][r]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * cl2;
+      const bool move = tmax > m_ref + 8.f;       // m_ref = -inf: any visible key moves it
+      if (__builtin_amdgcn_ballot_w64(move)) {
+        const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - tmax) : 1.f;   // m_ref = -inf -> 0
+        m_ref = move ? tmax : m_ref;
+        l_run *= alpha;
+        psum *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(a[db]), as_f16x8(bp), o[db], 0, 0, 0);
-      } else {
-        uint32_t hw[4], lw[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t ua = __float_as_uint(s[mb][r0 + 2 * j]), ub = __float_as_uint(s[mb][r0 + 2 * j + 1]);
-          hw[j] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
-          const f32x2 lo = {__uint_as_float(ua) - __uint_as_float(ua & 0xffff0000u),
-                            __uint_as_float(ub) - __uint_as_float(ub & 0xffff0000u)};
-          lw[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      }
+      // (a row with nothing visible yet keeps m_ref = -inf and uses 0, so exp2(-inf) = 0)
+      const float nm = m_ref == -INFINITY ? 0.f : -m_ref;
+      // l: the sum of the weights the value product uses (fp16 tiles: of the rounded ones, added
+      // pairwise by v_dot2_f32_f16 while they are packed)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[b][r], cl2, nm));
+          s[b][r] = e;
+          if constexpr (!decltype(f16)::value) psum += e;
         }
-        const u32x4 bh = {hw[0], hw[1], hw[2], hw[3]};
-        const u32x4 bl = {lw[0], lw[1], lw[2], lw[3]};
+      // O^T += V^T P^T over the pass's k-steps of 16 keys.  fp16 tiles: P rounded to nearest fp16
+      // (2^-11 relative, 2^-25 absolute below 2^-14), one product.  bf16 tiles: P = hi + lo with
+      // hi the truncated upper half and lo = P - hi (exact) rounded to bf16 by the hardware
+      // conversion, 2^-16 relative, two products.
+#pragma unroll
+      for (int ks2i = 0; ks2i < 2 * NB; ++ks2i) {
+        const int kst = 2 * NB * pass + ks2i, b = ks2i >> 1, r0 = 8 * (ks2i & 1);
+        u32x4 a[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[db]), as_bf16x8(bh), o[db], 0, 0, 0);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[db]), as_bf16x8(bl), o[db], 0, 0, 0);
+          const uint16_t* vrow = vt + (32 * db + col) * kVRow + 16 * kst + 4 * half;
+          const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
+          const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 8);
+          a[db] = u32x4{v0.x, v0.y, v1.x, v1.y};
+        }
+        if constexpr (decltype(f16)::value) {
+          uint32_t pw[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            pw[j] = f16x2_rne(s[b][r0 + 2 * j], s[b][r0 + 2 * j + 1]);
+            psum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pw[j]), f16x2{1.0f16, 1.0f16}, psum, false);
+          }
+          const u32x4 bp = {pw[0], pw[1], pw[2], pw[3]};
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(a[db]), as_f16x8(bp), o[db], 0, 0, 0);
+        } else {
+          uint32_t hw[4], lw[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t ua = __float_as_uint(s[b][r0 + 2 * j]), ub = __float_as_uint(s[b][r0 + 2 * j + 1]);
+            hw[j] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
+            const f32x2 lo = {__uint_as_float(ua) - __uint_as_float(ua & 0xffff0000u),
+                              __uint_as_float(ub) - __uint_as_float(ub & 0xffff0000u)};
+            lw[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+          }
+          const u32x4 bh = {hw[0], hw[1], hw[2], hw[3]};
+          const u32x4 bl = {lw[0], lw[1], lw[2], lw[3]};
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[db]), as_bf16x8(bh), o[db], 0, 0, 0);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[db]), as_bf16x8(bl), o[db], 0, 0, 0);
+          }
         }
       }
     }
@@ -489,11 +506,10 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
   if (t_vq > 0) {   // (uniform)
     constexpr int PER = kCodes * D * 2 / 16 / NTH;
     static_assert(PER * NTH * 16 == kCodes * D * 2, "codebook staging");
-    if constexpr (CBL) {   // the key codebook slice into LDS, 16 B per thread and step
+    // the key codebook slice into LDS, 16 B per thread and step
 #pragma unroll
-      for (int m = 0; m < PER; ++m)
-        reinterpret_cast<u32x4*>(cbk_l)[tid + NTH * m] = reinterpret_cast<const u32x4*>(slice_k)[tid + NTH * m];
-    }
+    for (int m = 0; m < PER; ++m)
+      reinterpret_cast<u32x4*>(cbk_l)[tid + NTH * m] = reinterpret_cast<const u32x4*>(slice_k)[tid + NTH * m];
     // the value slice against the fp16 window, once
     uint32_t mx = 0u, mn1 = 0xffffffffu;
 #pragma unroll
@@ -518,10 +534,7 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
   __builtin_amdgcn_s_waitcnt(kWaitVmem0);
   using f16_tag = std::integral_constant<bool, true>;
   using bf16_tag = std::integral_constant<bool, false>;
-  if constexpr (DBUF) {
-    // Two LDS buffers: tile k + 1 is stored, and tile k + 2 loaded into registers, while tile k
-    // is consumed; one barrier per tile.  Tiles k0, k0 + 1, ... in the tag's value format; the
-    // fp16 loop stops at a tile outside the fp16 window and returns its index (n_tiles at the end).
+  {
     auto run = [&](int k0, auto tag) -> int {
       constexpr bool AS = decltype(tag)::value;
       const int last = n_tiles - 1;
@@ -577,32 +590,8 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
       }
       return n_tiles;
     };
-    int k0 = 0;
-    if constexpr (F16) k0 = n_tiles > 0 && vq_f16 ? run(0, f16_tag{}) : 0;
+    const int k0 = n_tiles > 0 && vq_f16 ? run(0, f16_tag{}) : 0;
     if (k0 < n_tiles) run(k0, bf16_tag{});
-  } else {
-    // one LDS buffer: tile k is fetched, stored between two barriers and consumed (the fp16 loop
-    // stops at a tile outside the fp16 window, as above)
-    auto run1 = [&](int k0, auto tag) -> int {
-      constexpr bool AS = decltype(tag)::value;
-      if (has_vq) issue_idx(plan_idx(k0, fetch_page(k0)), ik_n, iv_n, ok_n);
-      for (int k = k0; k < n_tiles; ++k) {
-        fetch(k, ik_n, iv_n, ok_n);
-        if (has_vq && k + 1 < n_tiles) issue_idx(plan_idx(k + 1, fetch_page(k + 1)), ik_n, iv_n, ok_n);
-        __syncthreads();              // every wave is done with the previous tile
-        store(k, 0, tag);
-        __syncthreads();
-        if constexpr (AS) {
-          if (!tile_f16(0)) return k;   // (uniform)
-        }
-        const Tile tl = tile_of(k);
-        if (tl.seg != 3 || tl.start <= wave_last_qi) consume(tl.count, tl.seg == 3 ? tl.start : -1, tag);
-      }
-      return n_tiles;
-    };
-    int k0 = 0;
-    if (vq_f16) k0 = run1(0, f16_tag{});
-    if (k0 < n_tiles) run1(k0, bf16_tag{});
   }
 
   // ---- normalise and write: O^T register r of block db is channel 32db + 8(r/4) + 4half + r%4
@@ -626,10 +615,10 @@ __global__ void __launch_bounds__(ROT ? 256 : 512, ROT ? 2 : 1) extend_kernel(Ex
 template <int NG, int C>
 hipError_t launch_extend_variant(const ExtendParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.B * p.Hkv * p.row_blocks));
-  if (p.rot)
-    hipLaunchKernelGGL((extend_kernel<NG, C, true>), grid, dim3(256), 0, stream, p);   // 128 rows
+  if (p.rot)   // 256 rows per workgroup
+    hipLaunchKernelGGL((extend_kernel<NG, C, true>), grid, dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((extend_kernel<NG, C, false>), grid, dim3(512), 0, stream, p);  // 256 rows
+    hipLaunchKernelGGL((extend_kernel<NG, C, false>), grid, dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
