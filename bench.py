@@ -910,8 +910,10 @@ def main():
     ap.add_argument("--bf16-cache", action="store_true",
                     help="decode mode: the same kernel over an uncompressed bf16 cache (recent window = whole "
                          "context, no vector-quantized tokens), for the comparison with the packed cache")
-    ap.add_argument("--graph", action="store_true",
-                    help="decode mode: also capture one step in a HIP graph and time its replays (launch overhead)")
+    ap.add_argument("--eager", action="store_true",
+                    help="decode mode: the headline times the step's launches issued one by one; by default it "
+                         "times replays of the step captured in a HIP graph (the per-launch kernel times always "
+                         "come from the eager steps)")
     ap.add_argument("--lloyd", action="store_true",
                     help="time one weighted Lloyd iteration of one codebook set instead of the decode step "
                          "(default workload for this mode: deep4x32_h32_d128_b16_n8k)")
@@ -967,8 +969,9 @@ def main():
     step_ms = ev0.elapsed_time(ev1) / args.steps
     launch_us = np.array([a.elapsed_time(b) * 1e3 for a, b in events])
     graph = None
-    if args.graph:
-        # the same step captured once and replayed: the difference is the host launch overhead
+    if not args.eager:
+        # the same step captured once and replayed: a serving loop replays its decode step the same
+        # way; the difference to the eager step is the host launch overhead
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -989,6 +992,9 @@ def main():
         graph = {"ms_per_step": g_ms, "queries_per_s": wl.layers * wl.loops * wl.queries_per_launch / (g_ms * 1e-3),
                  "eager_minus_graph_ms": step_ms - g_ms}
         log(f"graph replay: {g_ms:.3f} ms per step (eager {step_ms:.3f} ms)")
+    eager_ms = step_ms
+    if graph is not None:
+        step_ms = graph["ms_per_step"]
     if plan:   # bytes of a launch averaged over the segments' launches
         ab_l = [algorithmic_bytes(wl.with_(chans=c, loop_group=G)) for segs in plan for n, c, G in segs
                 for _ in range(n)]
@@ -1039,9 +1045,10 @@ def main():
         "evict_launch_us": (float(np.mean([a.elapsed_time(b) * 1e3 for a, b in evict_events]))
                             if evict_events else None),
         "step_gbps": ab["total"] * wl.layers * wl.loops / (step_ms * 1e-3) / 1e9,
+        "step_timing": "eager" if graph is None else "hip_graph_replay",
+        "eager_ms_per_step": eager_ms,
+        "eager_queries_per_s": q_per_step / (eager_ms * 1e-3),
     }
-    if graph is not None:
-        rec["graph"] = graph
     if not args.no_cpu_baseline:
         # with a plan: the oracle on the workload of layer 0's first segment
         if plan or args.bf16_cache:
