@@ -174,9 +174,8 @@ __global__ void __launch_bounds__(512, 1) extend_kernel(ExtendParams p) {
 
   // ---- key tiles -----------------------------------------------------------------------------
   // Tile k of this workgroup: prefix tiles, vector-quantized tiles, recent tiles, then the
-  // chunk's tiles up to the workgroup's last row.  A tile's packed indices are fetched while the
-  // previous tile is consumed; its keys are then gathered, written to LDS and consumed.  (Two
-  // workgroups share a CU, so one's staging overlaps the other's products.)
+  // chunk's tiles up to the workgroup's last row.  While tile k is consumed, tile k + 1 is written
+  // to the other LDS buffer and the loads of the tiles after it are in flight (see the loop).
   const int t_pre = (n_prefix + kKT - 1) / kKT, t_vq = (n_vq + kKT - 1) / kKT, t_rec = (n_recent + kKT - 1) / kKT;
   const int t_ch = i_last / kKT + 1;
   const int n_tiles = t_pre + t_vq + t_rec + t_ch;

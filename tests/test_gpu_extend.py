@@ -42,8 +42,11 @@ CASES = {
 def _run_extend(name, mutate=None, abs_scale=1.0):
     """One extend launch of CASES[name] checked row by row against the oracle; mutate(case, kn, vn)
     may change the host values before they are uploaded."""
-    wl, layer, loop, lens, M, clens = CASES[name]
-    case = H.Case(wl, layer, loop, lens, seed=4)
+    _run_extend_case(name, *CASES[name], mutate=mutate, abs_scale=abs_scale)
+
+
+def _run_extend_case(name, wl, layer, loop, lens, M, clens, mutate=None, abs_scale=1.0, seed=4):
+    case = H.Case(wl, layer, loop, lens, seed=seed)
     B, Hq, Hkv, d = wl.batch, wl.q_heads, wl.kv_heads, wl.head_dim
     grp = Hq // Hkv
     kn = np.zeros((B, Hkv, M, d), np.uint16)
@@ -76,6 +79,8 @@ def _run_extend(name, mutate=None, abs_scale=1.0):
         n_pre, n_vq, n_rec = case.split[b]
         Mb = M if clens is None else clens[b]
         assert np.isnan(got[b, Mb:]).all(), "rows past the chunk length must stay untouched"
+        if Mb == 0:
+            continue
         for hq in range(Hq):
             h = hq // grp
             o_ref, _ = O.extend_attention(
