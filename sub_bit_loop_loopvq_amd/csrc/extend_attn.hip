@@ -127,8 +127,10 @@ __global__ void __launch_bounds__(512, 1) extend_kernel(ExtendParams p) {
 
   // ---- this lane's query row and its q operand (B of S^T = K Q^T) --------------------------
   const int row = row_ws + wave * 32 + col;
-  // the wave's last chunk token: a chunk tile that starts after it is hidden from all its rows
+  // the wave's first and last chunk tokens: a chunk tile that starts after the last is hidden from
+  // all its rows, one that ends at or before the first is visible to all of them
   const int wave_last_qi = min(Mb - 1, (row_ws + wave * 32 + 31) / grp);
+  const int wave_first_qi = (row_ws + wave * 32) / grp;
   const int qi = row / grp;                       // chunk token of the row
   const int hq = h * grp + row % grp;
   const bool active = qi < Mb;
@@ -403,7 +405,7 @@ __global__ void __launch_bounds__(512, 1) extend_kernel(ExtendParams p) {
         s[b] = acc;
       }
       // raw scores; token of register r of block mb: 32mb + 8(r/4) + 4half + r%4
-      if (count < kKT || chunk_j0 >= 0) {   // (uniform) a tile with keys to hide
+      if (count < kKT || (chunk_j0 >= 0 && chunk_j0 + kKT - 1 > wave_first_qi)) {   // (uniform) keys to hide
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
