@@ -374,9 +374,15 @@ loopvq_status loopvq_decode_attn_noalloc(const loopvq_config* cfg, const loopvq_
  * The other fields mean what they mean for decode (windows of the same (l, t),
  * pool, rot, softmax_scale); the codebooks come in the group-major layout of
  * loopvq_codebook_prepare_groups.  No workspace is needed.  The
- * kernel dequantizes 64-token tiles into LDS and runs both products on bf16 MFMAs,
- * splitting P (and a rotated q) into two bf16 parts so they keep fp32-level
- * accuracy. */
+ * kernel dequantizes 64-token tiles into LDS.  Scores run on bf16 MFMAs (a rotated q
+ * split into two bf16 parts, so fp32-level accuracy).  The value product runs on fp16
+ * MFMAs with the softmax weights rounded to fp16 (relative error at most 2^-11 per
+ * weight, 2^-25 absolute below 2^-14) while every value of the workgroup's tiles
+ * converts to fp16 exactly (zero or magnitude in [2^-17, 2^16)); from the first tile
+ * with another value on, and for the whole workgroup when the value codebook slice
+ * holds one, it runs on bf16 MFMAs with the weights split into two bf16 parts
+ * (2^-16 relative).  The normaliser is the sum of the weights the product used.
+ * Outputs stay within the attention tolerance (rel-L2 1e-3 per row) either way. */
 typedef struct loopvq_extend_args {
   int32_t layer;                /* l */
   int32_t loop;                 /* t (tau = t mod G, loop group t / G) */
