@@ -169,3 +169,64 @@ def test_group_major_codebooks_layout(c, G, d):
     want = bits.reshape(L, Jcb, Hkv, NG, K, G, c).transpose(0, 1, 2, 5, 3, 4, 6)
     got = d_grp.cpu().numpy().view(np.uint16).reshape(want.shape)
     assert np.array_equal(got, want)
+
+
+FULL_EXTEND = [
+    # (workload, chunk, sampled (sequence, q-head) pairs, sampled chunk rows)
+    (W.LAYER_4K, 512, [(0, 0), (17, 9), (31, 15)], [0, 37, 255, 256, 300]),   # both 256-row workgroups
+    (W.STACK_32K, 256, [(0, 0), (63, 15)], [0, 100, 255]),
+    (W.QUARTER_16K, 256, [(5, 3), (127, 15)], [0, 64, 255]),                   # rotated keys, c=8
+]
+
+
+@pytest.mark.parametrize("wl,M,samples,rows", FULL_EXTEND, ids=[w.name for w, _, _, _ in FULL_EXTEND])
+def test_extend_full_size_sampled(wl, M, samples, rows):
+    """An extend workload at its full shape (the launch bench.py --extend times for it), checked on
+    sampled rows of a few (sequence, head) pairs against the oracle.  The sampled pairs hold
+    generator indices packed by the oracle and generator windows and chunk rows; the other
+    sequences' pages are zero and their chunk rows plain normals (computed, not checked)."""
+    layer, loop = 0, 1
+    fc = H.FullCase(wl, layer, loop, samples)
+    fc.upload()
+    B, Hq, Hkv, d = wl.batch, wl.q_heads, wl.kv_heads, wl.head_dim
+    N = int(wl.context)
+    d_grp = []
+    for cb in (fc.cbk, fc.cbv):
+        d_cb = H.dev_u16(cb)
+        g = torch.empty_like(d_cb)
+        lvq.loopvq_codebook_prepare_groups(fc.cfg, d_cb, g)
+        d_grp.append(g)
+        del d_cb
+    rng = np.random.default_rng(77)
+    q = gen.to_bf16_bits(rng.normal(size=(B, M, Hq, d)))
+    kn = gen.to_bf16_bits(rng.normal(size=(B, Hkv, M, d)))
+    vn = gen.to_bf16_bits(rng.normal(size=(B, Hkv, M, d)))
+    for b, h in fc.pairs:
+        kn[b, h] = gen.kv_tokens(wl, 0, layer, b, h, N, N + M, loop, loop + 1, fc.sc)[:, 0]
+        vn[b, h] = gen.kv_tokens(wl, 1, layer, b, h, N, N + M, loop, loop + 1, fc.sc)[:, 0]
+    out = torch.full((B, M, Hq, d), float("nan"), dtype=torch.float32, device=H.DEV)
+    print(f"extend full size {wl.name}: {B} x {Hq} heads, cache {N}, chunk {M}", flush=True)
+    lvq.loopvq_extend_attn(fc.cfg, layer=layer, loop=loop, batch=B, chunk=M, q=H.dev_u16(q), k_new=H.dev_u16(kn),
+                           v_new=H.dev_u16(vn), seq_lens=fc.d_lens, max_seq_len=N, out=out, block_table=fc.d_bt,
+                           pool=fc.d_pool.data_ptr() - fc.pool_shift, max_pages_per_seq=fc.paging.max_pages,
+                           num_pages=fc.paging.num_pages, cb_k_grp=d_grp[0], cb_v_grp=d_grp[1],
+                           k_prefix=fc.d_win[0], v_prefix=fc.d_win[1], k_recent=fc.d_win[2], v_recent=fc.d_win[3],
+                           rot=fc.d_rot)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any().item(), "every row of the chunk is computed"
+    got = out.cpu().numpy().astype(np.float64)
+    del out
+    grp = Hq // Hkv
+    worst = 0.0
+    i_max = max(rows)
+    for b, hq in samples:
+        h = hq // grp
+        n_pre, _, n_rec = fc.split[b]
+        o_ref, _ = O.extend_attention(
+            H.f64(q[b, :i_max + 1, hq]), H.f64(fc.kp[b, h, :n_pre]), H.f64(fc.vp[b, h, :n_pre]), fc.idx[0, b, h],
+            fc.idx[1, b, h], H.codebooks_f64(fc.cbk, fc.l, fc.jc, h), H.codebooks_f64(fc.cbv, fc.l, fc.jc, h),
+            H.f64(fc.kr[b, h, :n_rec]), H.f64(fc.vr[b, h, :n_rec]), H.f64(kn[b, h, :i_max + 1]),
+            H.f64(vn[b, h, :i_max + 1]), fc.tau, wl.chans, 1.0 / np.sqrt(d), fc.rot)
+        rel, _ = H.check_attention(got[b, rows, hq], o_ref[rows])
+        worst = max(worst, rel)
+    print(f"  {len(samples) * len(rows)} sampled rows; worst rel-L2 {worst:.2e}", flush=True)
