@@ -395,3 +395,49 @@ def test_status_strings():
     for s, txt in [(0, "ok"), (-1, "invalid argument"), (-2, "unsupported variant"), (-3, "misaligned pointer"),
                    (-4, "workspace too small"), (-5, "HIP error"), (7, "unknown status")]:
         assert lvq.loopvq_status_string(s) == txt
+
+
+# ---------------------------------------------------------------------------------
+# The plain-C caller (tests/c_abi/decode_c.c): links against loopvq.h and the library
+# with gcc, and its host-side steps run without a GPU
+# ---------------------------------------------------------------------------------
+C_CALLER = os.path.join(ROOT, "tests", "c_abi", "decode_c")
+
+
+def _c_caller():
+    if not os.path.exists(C_CALLER):
+        import __graft_entry__
+        __graft_entry__.build_c_caller()
+    return C_CALLER
+
+
+def _write_c_args(path, cfg, **extra):
+    with open(os.path.join(path, "args.txt"), "w") as f:
+        for name, _ in cfg._fields_:
+            f.write(f"{name} {getattr(cfg, name)}\n")
+        for k, v in extra.items():
+            f.write(f"{k} {v}\n")
+
+
+C_EXTRA = dict(layer=0, loop=1, batch=2, max_pages_per_seq=4, max_seq_len=500, num_splits=0, num_pages=8,
+               pool_offset=0, pool_slice_bytes=0, softmax_scale=0.0, has_rot=0)
+
+
+def test_c_caller_rejects_bad_config_before_any_hip_call(tmp_path):
+    import subprocess
+    cfg = lvq.make_config(W.TINY.with_(loop_group=3))
+    _write_c_args(str(tmp_path), cfg, **C_EXTRA)
+    r = subprocess.run([_c_caller(), str(tmp_path)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1
+    assert "loopvq_config_check" in r.stderr and "returned invalid argument" in r.stderr
+    assert "multiple of loop_group" in r.stderr
+
+
+def test_c_caller_sizes_buffers_from_layout_query(tmp_path):
+    import subprocess
+    cfg = lvq.make_config(W.TINY)
+    _write_c_args(str(tmp_path), cfg, **C_EXTRA)
+    r = subprocess.run([_c_caller(), str(tmp_path)], capture_output=True, text=True, timeout=60)
+    lay = lvq.loopvq_layout_query(cfg, C_EXTRA["batch"], C_EXTRA["num_pages"])
+    assert r.returncode == 1 and "cannot open" in r.stderr and "q.bin" in r.stderr
+    assert f"0.500 bits per element, pool {lay.pool_bytes} bytes, page {lay.page_bytes} bytes" in r.stdout
