@@ -327,7 +327,7 @@ class FullCase:
                 self.d_pool[off:off + pb] = torch.from_numpy(pages[p]).to(DEV)
         torch.cuda.synchronize()
 
-    def gpu_decode(self, num_splits=0):
+    def gpu_decode(self, num_splits=0, scale=0.0):
         wl = self.wl
         out = torch.full((wl.batch, wl.q_heads, wl.head_dim), float("nan"), dtype=torch.float32, device=DEV)
         lse = torch.full((wl.batch, wl.q_heads), float("nan"), dtype=torch.float32, device=DEV)
@@ -342,12 +342,12 @@ class FullCase:
                                max_pages_per_seq=self.paging.max_pages, num_pages=self.paging.num_pages,
                                cb_k_prep=self.d_prep[0], cb_v_prep=self.d_prep[1], k_prefix=self.d_win[0],
                                v_prefix=self.d_win[1], k_recent=self.d_win[2], v_recent=self.d_win[3],
-                               rot=self.d_rot, lse=lse, num_splits=num_splits, workspace=ws,
+                               rot=self.d_rot, softmax_scale=scale, lse=lse, num_splits=num_splits, workspace=ws,
                                workspace_bytes=ws_bytes)
         torch.cuda.synchronize()
         return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
-    def oracle(self, b, hq):
+    def oracle(self, b, hq, scale=None):
         wl = self.wl
         h = hq // (wl.q_heads // wl.kv_heads)
         n_pre, _, n_rec = self.split[b]
@@ -355,4 +355,4 @@ class FullCase:
             f64(self.q[b, hq]), f64(self.kp[b, h, :n_pre]), f64(self.vp[b, h, :n_pre]),
             self.idx[0, b, h], self.idx[1, b, h], codebooks_f64(self.cbk, self.l, self.jc, h),
             codebooks_f64(self.cbv, self.l, self.jc, h), f64(self.kr[b, h, :n_rec]), f64(self.vr[b, h, :n_rec]),
-            self.tau, wl.chans, 1.0 / np.sqrt(wl.head_dim), self.rot)
+            self.tau, wl.chans, 1.0 / np.sqrt(wl.head_dim) if scale is None else scale, self.rot)
