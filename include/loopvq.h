@@ -309,8 +309,8 @@ typedef struct loopvq_decode_args {
   int32_t layer;                /* l in [0, L) */
   int32_t loop;                 /* t in [0, T) */
   int32_t batch;                /* B > 0 */
-  int32_t max_pages_per_seq;    /* with VQ rows, max_pages_per_seq * PT >= max_seq_len - P - R
-                                   (else LOOPVQ_ERR_INVALID_ARG) */
+  int32_t max_pages_per_seq;    /* with VQ rows, max_pages_per_seq * PT >= max_seq_len - P - R and
+                                   max_pages_per_seq * PT < 2^31 (else LOOPVQ_ERR_INVALID_ARG) */
   int32_t max_seq_len;          /* upper bound of seq_lens[] (sizes the split plan) */
   int32_t num_splits;           /* 0 = automatic, else 1..256 (at least the number a context of
                                    max_seq_len needs: one split holds at most 65,536 VQ rows) */
@@ -388,13 +388,14 @@ typedef struct loopvq_extend_args {
   int32_t loop;                 /* t (tau = t mod G, loop group t / G) */
   int32_t batch;                /* B */
   int32_t chunk;                /* M >= 1 */
-  int32_t max_pages_per_seq;
+  int32_t max_pages_per_seq;    /* as for decode */
   int32_t max_seq_len;          /* upper bound of seq_lens (cached tokens) */
   int64_t num_pages;
   const uint16_t* q;
   const uint16_t* k_new;
   const uint16_t* v_new;
-  const int32_t* seq_lens;      /* device [B] */
+  const int32_t* seq_lens;      /* device [B], each in [0, max_seq_len]; a length outside that range
+                                   (which the host cannot see) is clamped to it */
   const int32_t* chunk_lens;    /* device [B] or NULL */
   const int32_t* block_table;
   const uint8_t* pool;

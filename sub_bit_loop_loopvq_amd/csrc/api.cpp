@@ -217,6 +217,8 @@ loopvq_status decode_setup(const loopvq_config* cfg, const loopvq_decode_args* a
       return fail(LOOPVQ_ERR_INVALID_ARG, "block_table, pool and prepared codebooks must not be NULL");
     if (a->max_pages_per_seq < 1 || a->num_pages < 1)
       return fail(LOOPVQ_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
+    if (int64_t(a->max_pages_per_seq) * cfg->page_tokens > INT32_MAX)
+      return fail(LOOPVQ_ERR_INVALID_ARG, "max_pages_per_seq * page_tokens must stay below 2^31");
     if (!aligned(a->pool, 16) || !aligned(a->cb_k_prep, 16) || !aligned(a->cb_v_prep, 16))
       return fail(LOOPVQ_ERR_MISALIGNED, "pool and prepared codebooks must be 16-byte aligned");
   }
@@ -606,6 +608,14 @@ loopvq_status loopvq_extend_attn(const loopvq_config* cfg, const loopvq_extend_a
       return fail(LOOPVQ_ERR_INVALID_ARG, "block_table, pool and group-major codebooks must not be NULL");
     if (a->max_pages_per_seq < 1 || a->num_pages < 1)
       return fail(LOOPVQ_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
+    if (int64_t(a->max_pages_per_seq) * cfg->page_tokens > INT32_MAX)
+      return fail(LOOPVQ_ERR_INVALID_ARG, "max_pages_per_seq * page_tokens must stay below 2^31");
+    if (int64_t(a->max_seq_len) - cfg->prefix_tokens - cfg->recent_tokens >
+        int64_t(a->max_pages_per_seq) * cfg->page_tokens)
+      return fail(LOOPVQ_ERR_INVALID_ARG,
+                  "max_pages_per_seq (%d) pages of %d tokens cannot hold the %lld vector-quantized tokens of "
+                  "max_seq_len %d", a->max_pages_per_seq, cfg->page_tokens,
+                  (long long)(int64_t(a->max_seq_len) - cfg->prefix_tokens - cfg->recent_tokens), a->max_seq_len);
     if (!aligned(a->pool, 16) || !aligned(a->cb_k_grp, 16) || !aligned(a->cb_v_grp, 16))
       return fail(LOOPVQ_ERR_MISALIGNED, "pool and group-major codebooks must be 16-byte aligned");
   }

@@ -127,6 +127,7 @@ def _decode_kw(wl, **over):
     (dict(pool=None), lvq.LOOPVQ_ERR_INVALID_ARG),
     (dict(k_recent=None), lvq.LOOPVQ_ERR_INVALID_ARG),
     (dict(num_splits=300), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(max_pages_per_seq=2 ** 25), lvq.LOOPVQ_ERR_INVALID_ARG),     # 2^25 pages x 64 tokens = 2^31
     (dict(pool=FAKE + 8), lvq.LOOPVQ_ERR_MISALIGNED),
     (dict(k_prefix=FAKE + 2), lvq.LOOPVQ_ERR_MISALIGNED),
     (dict(out=FAKE + 2), lvq.LOOPVQ_ERR_MISALIGNED),
@@ -310,6 +311,8 @@ def _extend_kw(**over):
     (dict(k_new=None), lvq.LOOPVQ_ERR_INVALID_ARG),
     (dict(pool=None), lvq.LOOPVQ_ERR_INVALID_ARG),
     (dict(k_recent=None), lvq.LOOPVQ_ERR_INVALID_ARG),
+    (dict(max_pages_per_seq=2 ** 25), lvq.LOOPVQ_ERR_INVALID_ARG),     # 2^25 pages x 64 tokens = 2^31
+    (dict(max_pages_per_seq=6), lvq.LOOPVQ_ERR_INVALID_ARG),           # 428 VQ rows need 7 pages of 64
     (dict(q=FAKE + 8), lvq.LOOPVQ_ERR_MISALIGNED),
     (dict(out=FAKE + 4), lvq.LOOPVQ_ERR_MISALIGNED),
     (dict(v_new=FAKE + 2), lvq.LOOPVQ_ERR_MISALIGNED),
