@@ -207,3 +207,21 @@ def test_full_size_ragged_decode_sampled():
     for b, hq in samples:
         o_ref, lse_ref = fc.oracle(b, hq)
         H.check_attention(o[b, hq][None], o_ref[None], np.array([lse[b, hq]]), np.array([lse_ref]))
+
+
+@pytest.mark.parametrize("wl,loop", [(W.LAYER_4K, 2), (W.DEEP_8K, 17)], ids=["layer4k", "deep8k"])
+def test_full_launch_every_query(wl, loop):
+    """Every query of a full-size decode launch (512 queries of 4K or 8K tokens) against the oracle,
+    with the automatic split plan and with 3 splits."""
+    samples = [(b, hq) for b in range(wl.batch) for hq in range(wl.q_heads)]
+    _say(f"every query of {wl.name} loop={loop}")
+    fc = H.FullCase(wl, 0, loop, samples, seed=16)
+    fc.upload()
+    o_ref = np.zeros((wl.batch, wl.q_heads, wl.head_dim))
+    lse_ref = np.zeros((wl.batch, wl.q_heads))
+    for b, hq in samples:
+        o_ref[b, hq], lse_ref[b, hq] = fc.oracle(b, hq)
+    for S in (0, 3):
+        o, lse = fc.gpu_decode(num_splits=S)
+        rel, mx = H.check_attention(o, o_ref, lse, lse_ref)
+        _say(f"  splits {S}: rel-L2 {rel:.2e}, max-abs {mx:.2e}")
