@@ -6,17 +6,25 @@
  *   DIR/args.txt   whitespace-separated "name value" pairs: the loopvq_config
  *                  fields under their struct names, plus layer, loop, batch,
  *                  max_pages_per_seq, max_seq_len, num_splits, num_pages,
- *                  pool_offset (byte offset of pool.bin inside the whole pool),
- *                  softmax_scale and has_rot
- *   DIR/q.bin, lens.bin, bt.bin, pool.bin, cbk.bin, cbv.bin, kp.bin, vp.bin,
- *   kr.bin, vr.bin [, rot.bin]   raw little-endian arrays in the layouts loopvq.h
- *                  states (canonical codebooks, one (layer, loop step) of windows)
+ *                  pool_offset and pool_slice_bytes (the byte range of this
+ *                  (layer, loop group) inside the whole pool), softmax_scale,
+ *                  has_rot, and optionally encode (0 or 1) and n_rows
+ *   DIR/q.bin, lens.bin, bt.bin, cbk.bin, cbv.bin, kp.bin, vp.bin, kr.bin,
+ *   vr.bin [, rot.bin]   raw little-endian arrays in the layouts loopvq.h states
+ *                  (canonical codebooks, one (layer, loop step) of windows)
+ *   without encode: DIR/pool.bin, the packed pages of the pool range
+ *   with encode 1:  DIR/src_k.bin, src_v.bin (bf16 [G][n_rows][Hkv][d], the
+ *                  loop group's G loop steps of every row to encode),
+ *                  seq_id.bin and vq_pos.bin (int32 [n_rows]); the rows are
+ *                  encoded into a zeroed pool first, and the pool range is
+ *                  written to DIR/pool_out.bin
  * Writes DIR/out.bin (fp32 [B][Hq][d]) and DIR/lse.bin (fp32 [B][Hq]).
  *
  * The program owns every device buffer, as the library's conventions require:
  * it sizes them with loopvq_layout_query and loopvq_decode_attn_workspace,
- * prepares both codebook kinds with loopvq_codebook_prepare, runs one decode
- * launch, and also checks that a host-detectable mistake (batch 0) returns
+ * prepares both codebook kinds (and their norms) with loopvq_codebook_prepare,
+ * optionally encodes K and V rows with loopvq_encode, runs one decode launch,
+ * and also checks that a host-detectable mistake (batch 0) returns
  * LOOPVQ_ERR_INVALID_ARG with a message before any HIP call.
  * Exit status 0 on success, 1 on any failure (with a message on stderr).
  */
@@ -62,11 +70,21 @@ static void read_args(const char* dir) {
   fclose(f);
 }
 
-static double arg(const char* name) {
+static int find_arg(const char* name) {
   for (int i = 0; i < n_args; i++)
-    if (strcmp(arg_name[i], name) == 0) return arg_val[i];
-  FAIL("args.txt lacks %s", name);
-  return 0.0;
+    if (strcmp(arg_name[i], name) == 0) return i;
+  return -1;
+}
+
+static double arg(const char* name) {
+  const int i = find_arg(name);
+  if (i < 0) FAIL("args.txt lacks %s", name);
+  return arg_val[i];
+}
+
+static double arg_or(const char* name, double fallback) {
+  const int i = find_arg(name);
+  return i < 0 ? fallback : arg_val[i];
 }
 
 /* Read DIR/name into a new host buffer of exactly `bytes` bytes (the file must match). */
@@ -133,6 +151,7 @@ int main(int argc, char** argv) {
   const int64_t pool_offset = (int64_t)arg("pool_offset");
   const int64_t pool_slice = (int64_t)arg("pool_slice_bytes");
   const int has_rot = (int)arg("has_rot");
+  const int encode = (int)arg_or("encode", 0.0);
   const int64_t Hq = cfg.num_q_heads, d = cfg.head_dim;
 
   loopvq_layout lay;
@@ -155,21 +174,64 @@ int main(int argc, char** argv) {
   void* d_vr = upload(dir, "vr.bin", (size_t)lay.recent_elems * 2);
   void* d_rot = has_rot ? upload(dir, "rot.bin", (size_t)(d * d * 4)) : NULL;
 
-  /* the whole pool, zero except the slice the caller encoded */
+  /* the whole pool, zeroed (unwritten slots must be zero) */
   void* d_pool = NULL;
   HIP_OK(hipMalloc(&d_pool, (size_t)lay.pool_bytes));
   HIP_OK(hipMemset(d_pool, 0, (size_t)lay.pool_bytes));
-  {
+  if (!encode) {   /* the slice the caller packed */
     void* h = read_file(dir, "pool.bin", (size_t)pool_slice);
     if (pool_slice) HIP_OK(hipMemcpy((char*)d_pool + pool_offset, h, (size_t)pool_slice, hipMemcpyHostToDevice));
     free(h);
   }
 
-  /* decode-side codebook copies, one per kind */
+  /* decode-side codebook copies and squared norms, one per kind */
   void* d_prep[2];
+  void* d_norm[2];
   for (int kind = 0; kind < 2; kind++) {
     HIP_OK(hipMalloc(&d_prep[kind], (size_t)lay.codebook_elems * 2));
-    LVQ_OK(loopvq_codebook_prepare(&cfg, (const uint16_t*)d_cb[kind], (uint16_t*)d_prep[kind], NULL, NULL));
+    HIP_OK(hipMalloc(&d_norm[kind], (size_t)lay.norms_elems * 4));
+    LVQ_OK(loopvq_codebook_prepare(&cfg, (const uint16_t*)d_cb[kind], (uint16_t*)d_prep[kind], (float*)d_norm[kind],
+                                   NULL));
+  }
+
+  /* optionally: encode the rows of the loop group into the pool, K then V */
+  void *d_src[2] = {NULL, NULL}, *d_seq = NULL, *d_pos = NULL;
+  if (encode) {
+    const int32_t n_rows = (int32_t)arg("n_rows");
+    const int64_t G = cfg.loop_group, Hkv = cfg.num_kv_heads;
+    const size_t plane = (size_t)(n_rows * Hkv * d);
+    d_src[0] = upload(dir, "src_k.bin", (size_t)G * plane * 2);
+    d_src[1] = upload(dir, "src_v.bin", (size_t)G * plane * 2);
+    d_seq = upload(dir, "seq_id.bin", (size_t)n_rows * 4);
+    d_pos = upload(dir, "vq_pos.bin", (size_t)n_rows * 4);
+    for (int kind = 0; kind < 2; kind++) {
+      loopvq_encode_args ea;
+      memset(&ea, 0, sizeof ea);
+      ea.layer = (int32_t)arg("layer");
+      ea.loop_group = (int32_t)arg("loop") / cfg.loop_group;
+      ea.kind = kind;
+      ea.n_tokens = n_rows;
+      ea.src = (const uint16_t*)d_src[kind];
+      ea.stride_loop = (int64_t)plane;
+      ea.stride_token = Hkv * d;
+      ea.stride_head = d;
+      ea.seq_id = (const int32_t*)d_seq;
+      ea.vq_pos = (const int32_t*)d_pos;
+      ea.block_table = (const int32_t*)d_bt;
+      ea.batch = batch;
+      ea.max_pages_per_seq = max_pages;
+      ea.num_pages = num_pages;
+      ea.cb = (const uint16_t*)d_cb[kind];
+      ea.cb_norms = (const float*)d_norm[kind];
+      ea.pool = (uint8_t*)d_pool;
+      LVQ_OK(loopvq_encode(&cfg, &ea, NULL));
+    }
+    HIP_OK(hipDeviceSynchronize());
+    void* h = malloc(pool_slice ? (size_t)pool_slice : 1);
+    if (!h) FAIL("out of host memory");
+    if (pool_slice) HIP_OK(hipMemcpy(h, (char*)d_pool + pool_offset, (size_t)pool_slice, hipMemcpyDeviceToHost));
+    write_file(dir, "pool_out.bin", h, (size_t)pool_slice);
+    free(h);
   }
 
   /* outputs and workspace */
@@ -231,8 +293,8 @@ int main(int argc, char** argv) {
   free(h_out);
   free(h_lse);
 
-  void* bufs[] = {d_q, d_lens, d_bt, d_cb[0], d_cb[1], d_kp, d_vp, d_kr, d_vr, d_rot,
-                  d_pool, d_prep[0], d_prep[1], d_out, d_lse, d_ws};
+  void* bufs[] = {d_q, d_lens, d_bt, d_cb[0], d_cb[1], d_kp, d_vp, d_kr, d_vr, d_rot, d_pool, d_prep[0],
+                  d_prep[1], d_norm[0], d_norm[1], d_src[0], d_src[1], d_seq, d_pos, d_out, d_lse, d_ws};
   for (size_t i = 0; i < sizeof bufs / sizeof bufs[0]; i++)
     if (bufs[i]) HIP_OK(hipFree(bufs[i]));
   printf("decode_c: ok\n");
