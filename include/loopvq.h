@@ -371,6 +371,8 @@ loopvq_status loopvq_decode_attn_noalloc(const loopvq_config* cfg, const loopvq_
  *   chunk_lens   optional device int32 [B]: rows [0, chunk_lens[b]) of sequence b
  *                are computed (others untouched); NULL = all M
  *   out          device fp32 [B][M][Hq][d]
+ *   lse          optional device fp32 [B][M][Hq]: as for decode, the log-sum-exp of the row's
+ *                scores, for merging this attention with other parts
  * The other fields mean what they mean for decode (windows of the same (l, t),
  * pool, rot, softmax_scale); the codebooks come in the group-major layout of
  * loopvq_codebook_prepare_groups.  No workspace is needed.  The
@@ -408,6 +410,8 @@ typedef struct loopvq_extend_args {
   const float* rot;             /* [d][d] or NULL */
   float softmax_scale;          /* <= 0: 1/sqrt(d) */
   float* out;
+  float* lse;                   /* device fp32 [B][M][Hq] or NULL: ln sum_n exp(scale * q'.k_n) over
+                                   the keys the row sees (written for the computed rows only) */
 } loopvq_extend_args;
 
 loopvq_status loopvq_extend_attn(const loopvq_config* cfg, const loopvq_extend_args* args, void* stream);

@@ -74,7 +74,7 @@ class loopvq_extend_args(ctypes.Structure):
                 ("max_seq_len", _I32), ("num_pages", _I64), ("q", _P), ("k_new", _P), ("v_new", _P),
                 ("seq_lens", _P), ("chunk_lens", _P), ("block_table", _P), ("pool", _P), ("cb_k_grp", _P),
                 ("cb_v_grp", _P), ("k_prefix", _P), ("v_prefix", _P), ("k_recent", _P), ("v_recent", _P),
-                ("rot", _P), ("softmax_scale", _F32), ("out", _P)]
+                ("rot", _P), ("softmax_scale", _F32), ("out", _P), ("lse", _P)]
 
 
 EXPORTS = ("loopvq_config_check", "loopvq_bits_per_elem", "loopvq_layout_query", "loopvq_codebook_prepare",
@@ -299,13 +299,13 @@ def loopvq_decode_attn_noalloc(cfg, *, layer, loop, batch, q, seq_lens, max_seq_
 def loopvq_extend_attn(cfg, *, layer, loop, batch, chunk, q, k_new, v_new, seq_lens, max_seq_len, out,
                        chunk_lens=None, block_table=None, pool=None, max_pages_per_seq=0, num_pages=0,
                        cb_k_grp=None, cb_v_grp=None, k_prefix=None, v_prefix=None, k_recent=None, v_recent=None,
-                       rot=None, softmax_scale=0.0, stream=None) -> None:
+                       rot=None, softmax_scale=0.0, lse=None, stream=None) -> None:
     a = loopvq_extend_args(layer=layer, loop=loop, batch=batch, chunk=chunk, max_pages_per_seq=max_pages_per_seq,
                            max_seq_len=max_seq_len, num_pages=num_pages, q=_ptr(q), k_new=_ptr(k_new),
                            v_new=_ptr(v_new), seq_lens=_ptr(seq_lens), chunk_lens=_ptr(chunk_lens),
                            block_table=_ptr(block_table), pool=_ptr(pool), cb_k_grp=_ptr(cb_k_grp),
                            cb_v_grp=_ptr(cb_v_grp), k_prefix=_ptr(k_prefix), v_prefix=_ptr(v_prefix),
                            k_recent=_ptr(k_recent), v_recent=_ptr(v_recent), rot=_ptr(rot),
-                           softmax_scale=softmax_scale, out=_ptr(out))
+                           softmax_scale=softmax_scale, out=_ptr(out), lse=_ptr(lse))
     _check(lib().loopvq_extend_attn(ctypes.byref(cfg), ctypes.byref(a), _stream(stream)))
 

@@ -628,8 +628,8 @@ loopvq_status loopvq_extend_attn(const loopvq_config* cfg, const loopvq_extend_a
       !aligned(a->k_new, 16) || !aligned(a->v_new, 16) || !aligned(a->q, 16))
     return fail(LOOPVQ_ERR_MISALIGNED, "q, chunk and window buffers must be 16-byte aligned");
   if (!aligned(a->out, 16) || (a->rot && !aligned(a->rot, 4)) || !aligned(a->seq_lens, 4) ||
-      (a->chunk_lens && !aligned(a->chunk_lens, 4)))
-    return fail(LOOPVQ_ERR_MISALIGNED, "out (16 bytes), rot, seq_lens or chunk_lens misaligned");
+      (a->chunk_lens && !aligned(a->chunk_lens, 4)) || (a->lse && !aligned(a->lse, 4)))
+    return fail(LOOPVQ_ERR_MISALIGNED, "out (16 bytes), rot, seq_lens, chunk_lens or lse misaligned");
 
   const int j = a->loop / cfg->loop_group;
   const int jcb = cfg->codebook_per_loop_group ? j : 0;
@@ -669,6 +669,7 @@ loopvq_status loopvq_extend_attn(const loopvq_config* cfg, const loopvq_extend_a
   p.v_recent = a->v_recent;
   p.rot = a->rot;
   p.out = a->out;
+  p.lse = a->lse;
   const hipError_t e = lvq::launch_extend(p, z.ng, cfg->chans_per_group, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LOOPVQ_ERR_HIP, "extend_attn launch: %s", hipGetErrorString(e));
   return ok();

@@ -608,6 +608,9 @@ __global__ void __launch_bounds__(512, 1) extend_kernel(ExtendParams p) {
                           o[db][4 * r4 + 3] * inv};
         *reinterpret_cast<float4*>(orow + 32 * db + 8 * r4 + 4 * half) = v;
       }
+    // ln of the row's softmax normaliser: m_ref and l_tot are in log2 units and relative to m_ref
+    // (every computed row sees at least its own chunk key, so l_tot > 0)
+    if (p.lse && half == 0) p.lse[((int64_t)b * p.M + qi) * p.Hq + hq] = (m_ref + log2f(l_tot)) * 0.6931471805599453f;
   }
 }
 

@@ -89,6 +89,7 @@ struct ExtendParams {
   const uint16_t* v_recent;
   const float* rot;          // [d][d] or nullptr
   float* out;                // [B][M][Hq][d]
+  float* lse;                // [B][M][Hq] or nullptr
 };
 
 struct PrepareParams {

@@ -38,7 +38,7 @@ def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(lvq.loopvq_encode_args) == 4 * 4 + 8 + 3 * 8 + 3 * 8 + 4 + 4 + 8 + 5 * 8
     assert ctypes.sizeof(lvq.loopvq_decode_args) == 6 * 4 + 8 + 10 * 8 + 8 + 8 + 8 + 8
     assert ctypes.sizeof(lvq.loopvq_evict_args) == 4 + 4 + 8 + 12 * 8
-    assert ctypes.sizeof(lvq.loopvq_extend_args) == 6 * 4 + 8 + 14 * 8 + 8 + 8
+    assert ctypes.sizeof(lvq.loopvq_extend_args) == 6 * 4 + 8 + 14 * 8 + 8 + 8 + 8
     assert ctypes.sizeof(lvq.loopvq_lloyd_args) == 3 * 4 + 4 + 8 + 3 * 8 + 7 * 8 + 8 + 8
 
 
@@ -316,6 +316,7 @@ def _extend_kw(**over):
     (dict(q=FAKE + 8), lvq.LOOPVQ_ERR_MISALIGNED),
     (dict(out=FAKE + 4), lvq.LOOPVQ_ERR_MISALIGNED),
     (dict(v_new=FAKE + 2), lvq.LOOPVQ_ERR_MISALIGNED),
+    (dict(lse=FAKE + 2), lvq.LOOPVQ_ERR_MISALIGNED),
 ])
 def test_extend_rejects_before_launch(over, status):
     cfg = lvq.make_config(W.LAYER_4K)

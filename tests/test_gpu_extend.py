@@ -63,9 +63,10 @@ def _run_extend_case(name, wl, layer, loop, lens, M, clens, mutate=None, abs_sca
     case.d_pool.copy_(torch.from_numpy(case.oracle_pool(idx_of).reshape(-1)).to(H.DEV))
     q = gen.to_bf16_bits(np.random.default_rng(21).normal(size=(B, M, Hq, d)))
     out = torch.full((B, M, Hq, d), float("nan"), dtype=torch.float32, device=H.DEV)
+    lse = torch.full((B, M, Hq), float("nan"), dtype=torch.float32, device=H.DEV)
     print(f"extend {name}: lens {lens}, chunk {M}", flush=True)
     lvq.loopvq_extend_attn(case.cfg, layer=layer, loop=loop, batch=B, chunk=M, q=H.dev_u16(q), k_new=H.dev_u16(kn),
-                           v_new=H.dev_u16(vn), seq_lens=case.d_lens, max_seq_len=int(max(lens)), out=out,
+                           v_new=H.dev_u16(vn), seq_lens=case.d_lens, max_seq_len=int(max(lens)), out=out, lse=lse,
                            chunk_lens=H.dev_i32(clens) if clens is not None else None, block_table=case.d_bt,
                            pool=case.pool_base(), max_pages_per_seq=case.paging.max_pages,
                            num_pages=case.paging.num_pages, cb_k_grp=case.d_grp[0], cb_v_grp=case.d_grp[1],
@@ -73,24 +74,26 @@ def _run_extend_case(name, wl, layer, loop, lens, M, clens, mutate=None, abs_sca
                            v_recent=case.d_win[3], rot=case.d_rot)
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
+    got_lse = lse.cpu().numpy().astype(np.float64)
     scale = 1.0 / np.sqrt(d)
     checked, worst = 0, (0.0, 0.0)
     for b in range(B):
         n_pre, n_vq, n_rec = case.split[b]
         Mb = M if clens is None else clens[b]
         assert np.isnan(got[b, Mb:]).all(), "rows past the chunk length must stay untouched"
+        assert np.isnan(got_lse[b, Mb:]).all(), "lse of rows past the chunk length must stay untouched"
         if Mb == 0:
             continue
         for hq in range(Hq):
             h = hq // grp
-            o_ref, _ = O.extend_attention(
+            o_ref, lse_ref = O.extend_attention(
                 H.f64(q[b, :Mb, hq]), H.f64(case.kp[b, h, :n_pre]), H.f64(case.vp[b, h, :n_pre]), idx_of(0, b, h),
                 idx_of(1, b, h), H.codebooks_f64(case.cbk, layer, case.jc, h),
                 H.codebooks_f64(case.cbv, layer, case.jc, h), H.f64(case.kr[b, h, :n_rec]),
                 H.f64(case.vr[b, h, :n_rec]), H.f64(kn[b, h, :Mb]), H.f64(vn[b, h, :Mb]), case.tau, wl.chans, scale,
                 case.rot)
             # (abs_scale: the max-abs bound in units of the largest value magnitude, for values far from 1)
-            rel, mx = H.check_attention(got[b, :Mb, hq] / abs_scale, o_ref / abs_scale)
+            rel, mx = H.check_attention(got[b, :Mb, hq] / abs_scale, o_ref / abs_scale, got_lse[b, :Mb, hq], lse_ref)
             worst = (max(worst[0], rel), max(worst[1], mx))
             checked += Mb
     print(f"  {checked} rows checked; worst rel-L2 {worst[0]:.2e}, max-abs {worst[1]:.2e}", flush=True)
@@ -205,28 +208,32 @@ def test_extend_full_size_sampled(wl, M, samples, rows):
         kn[b, h] = gen.kv_tokens(wl, 0, layer, b, h, N, N + M, loop, loop + 1, fc.sc)[:, 0]
         vn[b, h] = gen.kv_tokens(wl, 1, layer, b, h, N, N + M, loop, loop + 1, fc.sc)[:, 0]
     out = torch.full((B, M, Hq, d), float("nan"), dtype=torch.float32, device=H.DEV)
+    lse = torch.full((B, M, Hq), float("nan"), dtype=torch.float32, device=H.DEV)
     print(f"extend full size {wl.name}: {B} x {Hq} heads, cache {N}, chunk {M}", flush=True)
     lvq.loopvq_extend_attn(fc.cfg, layer=layer, loop=loop, batch=B, chunk=M, q=H.dev_u16(q), k_new=H.dev_u16(kn),
-                           v_new=H.dev_u16(vn), seq_lens=fc.d_lens, max_seq_len=N, out=out, block_table=fc.d_bt,
+                           v_new=H.dev_u16(vn), seq_lens=fc.d_lens, max_seq_len=N, out=out, lse=lse,
+                           block_table=fc.d_bt,
                            pool=fc.d_pool.data_ptr() - fc.pool_shift, max_pages_per_seq=fc.paging.max_pages,
                            num_pages=fc.paging.num_pages, cb_k_grp=d_grp[0], cb_v_grp=d_grp[1],
                            k_prefix=fc.d_win[0], v_prefix=fc.d_win[1], k_recent=fc.d_win[2], v_recent=fc.d_win[3],
                            rot=fc.d_rot)
     torch.cuda.synchronize()
     assert not torch.isnan(out).any().item(), "every row of the chunk is computed"
+    assert not torch.isnan(lse).any().item(), "every row's lse is written"
     got = out.cpu().numpy().astype(np.float64)
-    del out
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    del out, lse
     grp = Hq // Hkv
     worst = 0.0
     i_max = max(rows)
     for b, hq in samples:
         h = hq // grp
         n_pre, _, n_rec = fc.split[b]
-        o_ref, _ = O.extend_attention(
+        o_ref, lse_ref = O.extend_attention(
             H.f64(q[b, :i_max + 1, hq]), H.f64(fc.kp[b, h, :n_pre]), H.f64(fc.vp[b, h, :n_pre]), fc.idx[0, b, h],
             fc.idx[1, b, h], H.codebooks_f64(fc.cbk, fc.l, fc.jc, h), H.codebooks_f64(fc.cbv, fc.l, fc.jc, h),
             H.f64(fc.kr[b, h, :n_rec]), H.f64(fc.vr[b, h, :n_rec]), H.f64(kn[b, h, :i_max + 1]),
             H.f64(vn[b, h, :i_max + 1]), fc.tau, wl.chans, 1.0 / np.sqrt(d), fc.rot)
-        rel, _ = H.check_attention(got[b, rows, hq], o_ref[rows])
+        rel, _ = H.check_attention(got[b, rows, hq], o_ref[rows], got_lse[b, rows, hq], lse_ref[rows])
         worst = max(worst, rel)
     print(f"  {len(samples) * len(rows)} sampled rows; worst rel-L2 {worst:.2e}", flush=True)
