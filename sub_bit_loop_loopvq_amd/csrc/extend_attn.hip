@@ -12,8 +12,10 @@
 //  * workgroup = 256 query rows (row = (chunk token, q-head of the kv-head)) of one
 //    (sequence, kv-head); 8 waves of 32 rows, one workgroup per CU.  Keys come in tiles of 64
 //    tokens, staged in LDS by the whole workgroup into two buffers (tile k + 1 while tile k is
-//    consumed): K as [token][d] bf16 rows and V transposed as [d][token] (rows padded so the
-//    MFMA operand reads hit distinct banks).  Vector-quantized tokens are dequantized on the
+//    consumed): K as [token][d] bf16 rows (padded so the MFMA operand reads hit distinct banks)
+//    and V as [token][d] rows too, whose 16-byte chunks are XOR-permuted per row; the value
+//    product reads its V^T operand with the transposing LDS read (ds_read_b64_tr_b16), so
+//    staging writes whole 16-byte chunks.  Vector-quantized tokens are dequantized on the
 //    way: the packed index byte of (token, group) selects the c channels of that group's
 //    loop-step slice; keys from the kv-head's key slice, copied to LDS once, values from the
 //    group-major codebook copy ([tau][g][k][i]) in L2.
@@ -23,7 +25,7 @@
 //    fp16 exactly, else with P split into two bf16 parts (hi + lo, 2^-16 relative).  The
 //    D-layout of S^T (lane = query row, registers = tokens) is directly the B operand of the
 //    second product once its 16 tokens are taken in the order the registers hold them; the
-//    V^T operand reads the same order.
+//    transposing reads gather the V^T operand in the same order.
 #include "lvq_common.h"
 
 namespace lvq {
@@ -36,12 +38,17 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kKT = 64;        // keys per tile
 // s_waitcnt immediate (gfx9 encoding): vector-memory count 0, the export and LDS/scalar counts
 // left at their maxima (no wait on them)
 constexpr int kWaitVmem0 = 0x0F70;
-constexpr int kVRow = kKT + 4; // bf16 per transposed V row (8 B of padding)
+// V tiles are row-major [key][d] with the 16-byte chunks of key row t XOR-permuted by vswz(t), so
+// that both the 16-byte row writes of the staging (8 consecutive keys, one chunk) and the
+// transposing operand reads (4 consecutive keys x 2 chunks per 16 lanes) hit 32 distinct banks.
+__device__ __forceinline__ int vswz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
@@ -91,7 +98,7 @@ __global__ void __launch_bounds__(512, 1) extend_kernel(ExtendParams p) {
   // codebook's loop-step slice of the kv-head in LDS (its K x d bf16, loaded once), so that the
   // dequantization of vector-quantized keys gathers from LDS instead of L2; q stays in registers.
   __shared__ __align__(16) uint16_t ks2[2][kKT * KROW];
-  __shared__ __align__(16) uint16_t vt2[2][D * kVRow];
+  __shared__ __align__(16) uint16_t vt2[2][kKT * D];
   __shared__ __align__(16) uint16_t cbk_l[kCodes * D];
   // The value tiles are staged as fp16 and the value product runs on fp16 MFMAs with P rounded
   // to fp16: one product instead of the bf16 hi + lo pair.  The first tile with a value outside
@@ -302,8 +309,8 @@ __global__ void __launch_bounds__(512, 1) extend_kernel(ExtendParams p) {
       }
     }
   };
-  // the registers of tile k into LDS: K as [token][d], V transposed [d][token]; entries past the
-  // tile's keys are written as zeros
+  // the registers of tile k into LDS: K and V as [token][d] (V chunks permuted by vswz); entries
+  // past the tile's keys are written as zeros
   // (values as fp16 when the tag is true, with the wave's window flag for buffer par)
   auto store = [&](int k, int par, auto as_f16) {
     constexpr bool AS = decltype(as_f16)::value;
@@ -327,15 +334,20 @@ __global__ void __launch_bounds__(512, 1) extend_kernel(ExtendParams p) {
         const uint32_t keep = ok_cur[m] ? 0xffffffffu : 0u;
 #pragma unroll
         for (int r = 0; r < GPI; ++r) {
-          const int g = g0 + r;
-          uint32_t* kd = reinterpret_cast<uint32_t*>(ks + t * KROW + g * C);
+          uint32_t* kd = reinterpret_cast<uint32_t*>(ks + t * KROW + (g0 + r) * C);
 #pragma unroll
-          for (int e = 0; e < C / 2; ++e) {
-            const uint32_t vw = vconv(fv[(m * GPI + r) * (C / 2) + e] & keep, std::false_type{});
-            kd[e] = fk[(m * GPI + r) * (C / 2) + e] & keep;
-            vt[(g * C + 2 * e) * kVRow + t] = (uint16_t)(vw & 0xffffu);
-            vt[(g * C + 2 * e + 1) * kVRow + t] = (uint16_t)(vw >> 16);
-          }
+          for (int e = 0; e < C / 2; ++e) kd[e] = fk[(m * GPI + r) * (C / 2) + e] & keep;
+        }
+        // the item's GPI * C value channels are whole 16-byte chunks of the key's V row
+        constexpr int NCH = GPI * C / 8;
+        static_assert(NCH * 8 == GPI * C, "value chunks");
+        const int c0 = g0 * C / 8;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = vconv(fv[m * GPI * (C / 2) + 4 * j + e] & keep, std::false_type{});
+          *reinterpret_cast<u32x4*>(vt + t * D + 8 * ((c0 + j) ^ vswz(t))) = w;
         }
       }
     } else {
@@ -346,12 +358,10 @@ __global__ void __launch_bounds__(512, 1) extend_kernel(ExtendParams p) {
         const uint32_t keep = t < tl.count ? 0xffffffffu : 0u;
         *reinterpret_cast<u32x4*>(ks + t * KROW + 8 * pc) =
             u32x4{fk[4 * m] & keep, fk[4 * m + 1] & keep, fk[4 * m + 2] & keep, fk[4 * m + 3] & keep};
+        u32x4 vw;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t vw = vconv(fv[4 * m + w] & keep, std::true_type{});
-          vt[(8 * pc + 2 * w) * kVRow + t] = (uint16_t)(vw & 0xffffu);
-          vt[(8 * pc + 2 * w + 1) * kVRow + t] = (uint16_t)(vw >> 16);
-        }
+        for (int w = 0; w < 4; ++w) vw[w] = vconv(fv[4 * m + w] & keep, std::true_type{});
+        *reinterpret_cast<u32x4*>(vt + t * D + 8 * (pc ^ vswz(t))) = vw;
       }
     }
     if constexpr (AS) {
@@ -374,6 +384,11 @@ __global__ void __launch_bounds__(512, 1) extend_kernel(ExtendParams p) {
     int lane_f = lane;
     if constexpr (ROT) asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_f));
     const int col = lane_f & 31, half = lane_f >> 5;
+    // transposing V reads: key row 4 half + s/4 of a k-step's 8-key half, logical chunk
+    // 4 db + 2 (lane / 16 % 2) + (s % 4) / 2, XOR-permuted by vswz of the row (= 2 (s/4) + half)
+    const int vs = lane_f & 15;
+    const int vkl = (2 * ((lane_f >> 4) & 1) + ((vs & 3) >> 1)) ^ (2 * (vs >> 2) + half);
+    const int vlane = (4 * half + (vs >> 2)) * 2 * D + 8 * (vs & 1);
     // NB 32-key blocks per pass: without a rotation both blocks of the tile in one pass; with one
     // (q' in two parts takes 32 more registers), one block per pass, so that the scores and the
     // key operands of only half the tile are live at once.
@@ -451,13 +466,16 @@ __global__ void __launch_bounds__(512, 1) extend_kernel(ExtendParams p) {
 #pragma unroll
       for (int ks2i = 0; ks2i < 2 * NB; ++ks2i) {
         const int kst = 2 * NB * pass + ks2i, b = ks2i >> 1, r0 = 8 * (ks2i & 1);
+        // V^T operand by transposing reads: lane s of each 16 points at 4 channels of key row
+        // 16 kst + 8 rd + 4 half + s/4, and receives its own channel of those 4 keys
         u32x4 a[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const uint16_t* vrow = vt + (32 * db + col) * kVRow + 16 * kst + 4 * half;
-          const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 8);
-          a[db] = u32x4{v0.x, v0.y, v1.x, v1.y};
+          const uint8_t* vb = reinterpret_cast<const uint8_t*>(vt) + vlane + 16 * ((4 * db) ^ vkl) + 32 * D * kst;
+          const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb));
+          const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + 16 * D));
+          const uint2 u0 = __builtin_bit_cast(uint2, r0), u1 = __builtin_bit_cast(uint2, r1);
+          a[db] = u32x4{u0.x, u0.y, u1.x, u1.y};
         }
         if constexpr (decltype(f16)::value) {
           uint32_t pw[4];
