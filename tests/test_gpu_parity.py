@@ -178,11 +178,16 @@ FULL = [
     (W.QUARTER_16K, 9, 1),
     (W.DEEP_8K, 2, 29),
     (W.DEEP_8K.with_(codebook_per_loop_group=True), 3, 21),
+    # the other built (c, G) shapes at the deep workload's full size: 8 channels x 2 loop steps
+    # (0.5 bit, 16 groups) and 4 channels x 8 loop steps (0.25 bit, 32 groups)
+    (W.DEEP_8K.with_(chans=8, loop_group=2), 1, 13),
+    (W.DEEP_8K.with_(loop_group=8), 2, 30),
 ]
 
 
 @pytest.mark.parametrize("wl,layer,loop", FULL, ids=[w.name + ("_cbj" if w.codebook_per_loop_group else "")
-                                                     for w, _, _ in FULL])
+                                                     + (f"_c{w.chans}g{w.loop_group}" if (w.chans, w.loop_group)
+                                                        != (4, 4) else "") for w, _, _ in FULL])
 def test_full_size_decode_sampled(wl, layer, loop):
     rng = np.random.default_rng(wl.wid)
     samples = [(int(rng.integers(wl.batch)), int(rng.integers(wl.q_heads))) for _ in range(6)]
