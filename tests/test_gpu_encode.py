@@ -38,10 +38,12 @@ def test_device_generator_matches_host(wl, kind, layer):
         assert np.array_equal(got[:, 0, h], want.transpose(1, 0, 2))
 
 
-def test_full_size_encode_sampled():
-    """65536 tokens x 32 kv-heads x 32 groups of one (layer, loop group), keys and values."""
-    wl = W.DEEP_8K
-    layer, j = 1, 5
+@pytest.mark.parametrize("c,G", [(4, 4), (8, 2), (4, 8)], ids=["c4g4", "c8g2", "c4g8"])
+def test_full_size_encode_sampled(c, G):
+    """65536 tokens x 32 kv-heads x all groups of one (layer, loop group), keys and values, at the
+    deep workload's (c, G) = (4, 4) and at the other built shapes (8, 2) and (4, 8)."""
+    wl = W.DEEP_8K.with_(chans=c, loop_group=G)
+    layer, j = 1, min(5, wl.loop_groups - 1)
     per_seq = wl.encode_tokens // wl.batch          # 4096 tokens per sequence
     rows = wl.encode_tokens
     Hkv, d, G, P = wl.kv_heads, wl.head_dim, wl.loop_group, wl.prefix
