@@ -67,3 +67,46 @@ def test_noalloc_equals_workspace_entry_point(splits_big, splits_small):
         assert np.array_equal(lse, lse_ref), f"lse differs (batch {case.wl.batch}, splits {S})"
     _say("  ok")
 
+
+
+def test_noalloc_replays_under_graph_capture():
+    """Captured in a HIP graph (the use the entry point is for), the allocation-free decode replays
+    to its eager result bit for bit, three times, with eager calls of the same entry point (on
+    another input) between the replays; 7 splits, so the static partials array is used."""
+    _say("noalloc under graph capture")
+    case = _setup(BIG, [900, 1, 73, 300, 650, 899])
+    other = _setup(SMALL, [400, 150])
+    o_ref, lse_ref = _noalloc(case, 7)
+    wl = case.wl
+    out = torch.full((wl.batch, wl.q_heads, wl.head_dim), float("nan"), dtype=torch.float32, device=H.DEV)
+    lse = torch.full((wl.batch, wl.q_heads), float("nan"), dtype=torch.float32, device=H.DEV)
+
+    def call():
+        lvq.loopvq_decode_attn_noalloc(case.cfg, layer=case.l, loop=case.t, batch=wl.batch, q=case.d_q,
+                                       seq_lens=case.d_lens, max_seq_len=int(case.lens.max()), out=out,
+                                       block_table=case.d_bt, pool=case.pool_base(),
+                                       max_pages_per_seq=case.paging.max_pages, num_pages=case.paging.num_pages,
+                                       cb_k_prep=case.d_prep[0], cb_v_prep=case.d_prep[1], k_prefix=case.d_win[0],
+                                       v_prefix=case.d_win[1], k_recent=case.d_win[2], v_recent=case.d_win[3],
+                                       rot=case.d_rot, lse=lse, num_splits=7)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()                        # warm-up on the capture's stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for _ in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().astype(np.float64), o_ref), "graph replay output differs"
+        assert np.array_equal(lse.cpu().numpy().astype(np.float64), lse_ref), "graph replay lse differs"
+        _noalloc(other, 3)            # an eager call between replays rewrites the static array
+    del g
+    torch.cuda.empty_cache()
+    _say("  ok")
